@@ -1,0 +1,228 @@
+/*
+ * vc.h — C ABI of the draft/verify attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the GPU hot path of VeriCache ("VeriCache: Turning Lossy KV Cache into
+ * Lossless LLM Inference", technical review page, §Draft–Verify Pipeline): a drafter decodes
+ * with a compressed KV cache, a verifier attends with the full KV cache over the drafted block
+ * in one parallel pass, and a greedy accept keeps the longest agreeing prefix.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers marked (device) are device memory on the current HIP device; (host) are host memory.
+ *   All tensors are caller-owned; the library never frees caller memory and allocates nothing
+ *   except where a call says so.
+ * - Calls are asynchronous on the given stream (a hipStream_t passed as void*; NULL = default
+ *   stream) and never synchronise, except vc_stage_kv's event which the caller waits on.
+ * - Every call validates its arguments on the host first.  On failure it returns a negative
+ *   vc_status, enqueues nothing and records a message readable with vc_last_error() (per
+ *   thread).  HIP errors are reported as VC_EHIP.  Nothing throws across the ABI.
+ * - KV caches are paged: 16-token blocks ("pages") in a pool shared by all requests, with a
+ *   per-request page table giving the physical block of each logical page; every layer of the
+ *   pool uses the same table.  Positions past a request's length inside its last page, and
+ *   drafted-block rows past the last visible one, may hold any bits (even NaN): they never
+ *   reach a result.
+ * - Shapes: head_dim d in {64, 128}; G = Hq / Hkv query heads per KV head (1..16); query head h
+ *   reads KV head h / G.
+ */
+#ifndef VC_H
+#define VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VC_OK = 0,
+  VC_EINVAL = -1,       /* bad argument; nothing was enqueued */
+  VC_ENOSPACE = -2,     /* workspace too small; nothing was enqueued */
+  VC_EHIP = -3,         /* a HIP runtime call failed */
+  VC_EUNSUPPORTED = -4  /* valid but not implemented (e.g. head_dim 96) */
+} vc_status;
+
+#define VC_BLOCK_TOKENS 16   /* tokens per KV page */
+#define VC_MAX_REQS 64       /* requests per attention launch */
+#define VC_MAX_ROWS 64       /* drafted rows per request */
+#define VC_KIVI_GROUP 32     /* KIVI quantisation group (tokens for keys, channels for values) */
+
+/* Kind of work of one request in an attention launch. */
+#define VC_VERIFY 0  /* x query rows, full context + causal drafted block (MFMA row tiles) */
+#define VC_DRAFT 1   /* one decode step (rows*G <= 16), compressed context + drafted rows 0..q0 */
+
+typedef struct {
+  int32_t num_layers;    /* L: layer slices stored in every pool */
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t max_rows;      /* XMAX: drafted-row capacity of q/blk/out tensors; multiple of 16, <= 64 */
+} vc_shape;
+
+/*
+ * A paged KV pool (device memory).  nb = num_blocks, Hkv and d as in vc_shape.
+ *
+ * bits == 16 (bf16 cache: the full KV, or a token-dropped compact cache):
+ *   k     bf16 [L][nb][Hkv][16 tokens][d]        (token-major page)
+ *   v     bf16 [L][nb][Hkv][d][16 tokens]        (channel-major page)
+ * bits == 2 or 4 (KIVI-style cache: keys quantised per channel over groups of 32 consecutive
+ * stored tokens, values per token over groups of 32 consecutive channels; x^ = code*scale+zero):
+ *   k     uint32 [L][nb][Hkv][16 tokens][d*bits/32]   codes of each token row: channel c is code
+ *         u = c % (32/bits) of word c / (32/bits), stored at bit (u%2)*16 + bits*(u/2) (the two
+ *         halves of a word hold the even and the odd codes, so one shift and mask yields a pair)
+ *   v     uint32 [L][nb][Hkv][d][16*bits/32]          codes of each channel's 16 tokens, same
+ *         packing with the token index in place of the channel
+ *   k_sz  fp16 [L][nb][Hkv][d][2]   (scale, zero) of each channel for the 32-token group made of
+ *         logical pages 2j and 2j+1, stored in the block of page 2j (odd pages' entries unused)
+ *   v_sz  fp16 [L][nb][Hkv][d/32][16][2]   (scale, zero) per channel group and token
+ */
+typedef struct {
+  int32_t bits;                /* 16, 2 or 4 */
+  int32_t max_pages;           /* row stride of page_table */
+  int64_t num_blocks;          /* nb: physical blocks per layer */
+  const int32_t* page_table;   /* (device) int32 [rows][max_pages]; -1 = no block */
+  const void* k;               /* (device) see above */
+  const void* v;               /* (device) */
+  const void* k_sz;            /* (device) KIVI only, else NULL */
+  const void* v_sz;            /* (device) KIVI only, else NULL */
+} vc_pool;
+
+/*
+ * One request of an attention launch.  Query rows are block positions q0 .. q0+rows-1 of request
+ * slot `slot`; a row at block position j attends to ctx_len context tokens of pool `pool`
+ * (logical pages from page-table row `page_row`) plus drafted-block rows 0..j.
+ * Verify pass (VeriCache review, §Draft–Verify Pipeline step 4): kind VC_VERIFY, q0 = 0,
+ * rows = x, the full pool.  Draft step i (steps 1–2): kind VC_DRAFT, q0 = i, rows = 1, the
+ * compressed pool.
+ */
+typedef struct {
+  int32_t slot;      /* request slot in q / blk / out (0 <= slot < batch) */
+  int32_t pool;      /* index into the pools array of the call */
+  int32_t ctx_len;   /* context tokens visible in that pool (>= 0) */
+  int32_t page_row;  /* row of that pool's page table */
+  int32_t q0;        /* block position of the first query row */
+  int32_t rows;      /* query rows (>= 1); q0 + rows <= max_rows */
+  int32_t kind;      /* VC_VERIFY or VC_DRAFT */
+} vc_req;
+
+/*
+ * Common tensors of the attention calls (device):
+ *   q      bf16 [batch][L][max_rows][Hq][d]      query of drafted-block position i at row i
+ *   blk_k  bf16 [batch][L][Hkv][max_rows/16][16][d]   the drafted block's own keys (pages)
+ *   blk_v  bf16 [batch][L][Hkv][max_rows/16][d][16]   and values (channel-major pages)
+ *   out    fp32 [batch][L][max_rows][Hq][d]      attention output; only rows q0..q0+rows-1 of
+ *          each request are written
+ *   workspace: device scratch for split-context partial results, at least
+ *          vc_attn_workspace_size() bytes for the same arguments; may be NULL when that is 0.
+ * Attention (VeriCache review, §Prerequisites, attention equation): softmax(q k^T / sqrt(d)) v,
+ * fp32 accumulation, bf16 inputs, softmax weights rounded to bf16 for the value product.
+ * split_pages: context pages per split (multiple of 4), 0 = automatic.
+ */
+
+/* Bytes of workspace an attention call with these requests needs (0 if no split). */
+size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req* reqs /* host */,
+                              int split_pages);
+
+/* Verify pass: every request is VC_VERIFY over `full` (bf16 pool); req.pool is ignored. */
+int vc_verify_attn(const vc_shape* shape, int num_reqs, const vc_req* reqs /* host */,
+                   const void* q, const void* blk_k, const void* blk_v, const vc_pool* full /* host struct */,
+                   float* out, void* workspace, size_t workspace_bytes, int split_pages, void* stream);
+
+/* Draft step: every request is VC_DRAFT over `comp` (bf16 token-dropped or KIVI pool). */
+int vc_draft_attn(const vc_shape* shape, int num_reqs, const vc_req* reqs /* host */,
+                  const void* q, const void* blk_k, const void* blk_v, const vc_pool* comp /* host struct */,
+                  float* out, void* workspace, size_t workspace_bytes, int split_pages, void* stream);
+
+/* One launch over a mixed list: each request names its pool (0 <= pool < num_pools <= 4) and
+ * kind, so drafting and verifying requests of a batch run together (VeriCache review,
+ * §The two design principles, P1: every iteration mixes drafters and verifiers). */
+int vc_attn_mixed(const vc_shape* shape, int num_reqs, const vc_req* reqs /* host */,
+                  const void* q, const void* blk_k, const void* blk_v,
+                  int num_pools, const vc_pool* pools /* host array */,
+                  float* out, void* workspace, size_t workspace_bytes, int split_pages, void* stream);
+
+/*
+ * Greedy accept (VeriCache review, §Draft–Verify Pipeline steps 5–6) for n_inst independent
+ * drafted blocks.  For instance i: x[i] drafted rows (1..max_x), xv[i] verifier rows (x[i], or
+ * x[i]+1 where the extra row gives the bonus token; at most max_xv).  Logits rows are contiguous
+ * over `vocab`:
+ *   draft_logits  fp32 [n_inst][max_x][vocab]     row j = draft step j
+ *   verify_logits fp32 [n_inst][max_xv][vocab]    row j = verifier prediction for slot j
+ * Outputs (device): draft_tok int32 [n_inst][max_x], verify_tok int32 [n_inst][max_xv] (argmax,
+ * ties to the lowest id; unused rows -1); accept_len int32 [n_inst] = first j with
+ * draft_tok != verify_tok, else x; next_tok int32 [n_inst] = verify_tok[accept_len] if that row
+ * exists, else -1.  x and xv are device arrays (values are clamped to [0, max_x], [0, max_xv]).
+ * Logits must be finite.
+ */
+int vc_accept(int n_inst, int max_x, int max_xv, int vocab, const int32_t* x, const int32_t* xv,
+              const float* draft_logits, const float* verify_logits,
+              int32_t* draft_tok, int32_t* verify_tok, int32_t* accept_len, int32_t* next_tok,
+              void* stream);
+
+/*
+ * LM-head stand-in used to turn attention outputs into logits: z[r][v] = sum_w o[r][w] * W_u[w][v]
+ * (fp32 accumulate).  o fp32 [rows][width] with row stride ld_o floats; w_u bf16 [width][vocab];
+ * z fp32 [rows][vocab].  VeriCache review, §Draft–Verify Pipeline: argmax over the logits of
+ * each position.
+ */
+int vc_logits(int rows, int width, int vocab, const float* o, int64_t ld_o, const void* w_u,
+              float* z, void* stream);
+
+/* ---- Building caches (untimed preparation; VeriCache review, §Compression Method Integration:
+ *      compress() runs once, offline, before serving) ---- */
+
+/*
+ * Write one layer of a bf16 paged pool from a dense tensor.
+ * src bf16 [batch][Hkv][src_rows][d] (device): token t of request r is src[r][g][t]; only tokens
+ * t < lens[r] are written (lens: host int32 [batch]); page_row of request r is r.
+ * which: 0 = keys (token-major pages), 1 = values (channel-major pages).
+ */
+int vc_pack_bf16(const vc_shape* shape, int batch, const int32_t* lens /* host */, int layer,
+                 const void* src, int64_t src_rows, const vc_pool* pool, int which, void* stream);
+
+/*
+ * Token-drop selection: for every (request r, layer l, kv head g) keep positions
+ * [n_r - recent_r, n_r) plus the top_r older positions by score (larger first, ties to the lower
+ * position), written ascending to kept[r][l][g][0 .. recent_r + top_r) (int32, device, row
+ * stride kept_stride).  scores uint32 [batch][L][Hkv][score_stride] (device).
+ * lens/recent/top: host int32 [batch] (recent, top clamped to n_r).
+ */
+int vc_select_kept(const vc_shape* shape, int batch, const int32_t* lens, const int32_t* recent,
+                   const int32_t* top, const uint32_t* scores, int64_t score_stride,
+                   int32_t* kept, int64_t kept_stride, void* stream);
+
+/*
+ * Build a compressed pool for layer range [0, L) from a bf16 source pool:
+ * token j of request r in `dst` comes from source position kept[r][l][g][j] (or position j when
+ * kept is NULL), for j < comp_lens[r] (host int32 [batch]).  src page_row = dst page_row = r.
+ * dst->bits 16: copy (token drop).  dst->bits 2/4: KIVI-style quantisation of the gathered
+ * sequence (keys per channel over groups of 32 tokens, values per token over groups of 32
+ * channels; scale = fp16(RNE((max-min)/(2^b-1))), zero = fp16(RNE(min)), code =
+ * clamp(RNE((x-zero)/scale), 0, 2^b-1), 0 when scale is 0; all in fp64).
+ */
+int vc_compress(const vc_shape* shape, int batch, const int32_t* comp_lens /* host */,
+                const vc_pool* src, const int32_t* kept, int64_t kept_stride,
+                const vc_pool* dst, void* stream);
+
+/* ---- Staging the full KV into HBM (VeriCache review, §KV Swap Scheduling: the full cache is
+ *      reloaded from host memory ahead of its verify, overlapped with drafting) ---- */
+
+/*
+ * Copy `bytes` from pinned host memory (allocated with hipHostMalloc or equivalent) to device
+ * memory on `side_stream`, then record `event` (a hipEvent_t as void*, may be NULL) on it.
+ * The caller makes its verify stream wait on the event.  Nothing is synchronised here.
+ */
+int vc_stage_kv(void* dst_device, const void* src_pinned_host, size_t bytes, void* side_stream,
+                void* event);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* vc_last_error(void);
+
+/* Library version, e.g. "vc 0.1 gfx950". */
+const char* vc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VC_H */

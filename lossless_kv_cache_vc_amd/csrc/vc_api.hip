@@ -1,0 +1,294 @@
+// Host side of the C ABI: argument validation, launch planning and the exported entry points.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "vc_internal.h"
+
+namespace vc {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VC_OK;
+  return fail(VC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+static int check_shape(const vc_shape* s) {
+  if (!s) return fail(VC_EINVAL, "shape is NULL");
+  if (s->num_layers < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(VC_EINVAL, "layers and head counts must be >= 1");
+  if (s->num_q_heads % s->num_kv_heads)
+    return fail(VC_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (s->num_q_heads / s->num_kv_heads > 16)
+    return fail(VC_EUNSUPPORTED, "more than 16 query heads per kv head");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(VC_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (s->max_rows < 16 || s->max_rows > VC_MAX_ROWS || s->max_rows % 16)
+    return fail(VC_EINVAL, "max_rows must be a multiple of 16 in [16, 64]");
+  return VC_OK;
+}
+
+static int check_pool(const vc_pool* p, int head_dim, const char* name) {
+  char buf[160];
+  if (!p) {
+    snprintf(buf, sizeof buf, "%s pool is NULL", name);
+    return fail(VC_EINVAL, buf);
+  }
+  if (p->bits != 16 && p->bits != 2 && p->bits != 4) {
+    snprintf(buf, sizeof buf, "%s pool: bits must be 16, 2 or 4 (got %d)", name, p->bits);
+    return fail(VC_EINVAL, buf);
+  }
+  if (!p->page_table || !p->k || !p->v) {
+    snprintf(buf, sizeof buf, "%s pool: page_table, k and v must be set", name);
+    return fail(VC_EINVAL, buf);
+  }
+  if (p->bits != 16 && (!p->k_sz || !p->v_sz)) {
+    snprintf(buf, sizeof buf, "%s pool: KIVI pools need k_sz and v_sz", name);
+    return fail(VC_EINVAL, buf);
+  }
+  if (p->num_blocks < 1 || p->max_pages < 1) {
+    snprintf(buf, sizeof buf, "%s pool: num_blocks and max_pages must be >= 1", name);
+    return fail(VC_EINVAL, buf);
+  }
+  (void)head_dim;
+  return VC_OK;
+}
+
+static PoolDev to_dev(const vc_pool& p) {
+  PoolDev d;
+  d.k = static_cast<const uint8_t*>(p.k);
+  d.v = static_cast<const uint8_t*>(p.v);
+  d.ksz = static_cast<const uint8_t*>(p.k_sz);
+  d.vsz = static_cast<const uint8_t*>(p.v_sz);
+  d.page_table = p.page_table;
+  d.nblk = p.num_blocks;
+  d.max_pages = p.max_pages;
+  d.bits = p.bits;
+  return d;
+}
+
+static int auto_chunk(const vc_shape* s, int nreq, const vc_req* reqs) {
+  // aim for about 2048 work items (8 per CU) so the 256 CUs see several waves of work-groups
+  const int G = s->num_q_heads / s->num_kv_heads;
+  int64_t total = 0;
+  for (int i = 0; i < nreq; ++i) {
+    const int pages = (reqs[i].ctx_len + kBlock - 1) / kBlock;
+    const int nrg = reqs[i].kind == VC_VERIFY ? (reqs[i].rows * G + 127) / 128 : 1;
+    total += (int64_t)s->num_layers * s->num_kv_heads * nrg * pages;
+  }
+  int64_t chunk = (total + 2047) / 2048;
+  chunk = std::max<int64_t>(16, (chunk + 3) / 4 * 4);
+  return (int)std::min<int64_t>(chunk, 1 << 28);
+}
+
+int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const vc_pool* pools,
+              int split_pages, AttnArgs* args, Plan* plan) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (nreq < 0 || nreq > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 64]");
+  if (nreq > 0 && !reqs) return fail(VC_EINVAL, "reqs is NULL");
+  if (npools < 1 || npools > kMaxPools) return fail(VC_EINVAL, "num_pools must be in [1, 4]");
+  if (split_pages < 0 || split_pages % 4) return fail(VC_EINVAL, "split_pages must be a multiple of 4");
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int D = s->head_dim;
+  memset(args, 0, sizeof(*args));
+  for (int i = 0; i < npools; ++i) args->pools[i] = to_dev(pools[i]);
+  std::vector<char> pool_used(npools, 0);
+  const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs);
+  int64_t items = 0, part = 0;
+  plan->any_split = 0;
+  for (int i = 0; i < nreq; ++i) {
+    const vc_req& r = reqs[i];
+    char buf[200];
+    if (r.kind != VC_VERIFY && r.kind != VC_DRAFT) {
+      snprintf(buf, sizeof buf, "request %d: kind must be VC_VERIFY or VC_DRAFT", i);
+      return fail(VC_EINVAL, buf);
+    }
+    if (r.pool < 0 || r.pool >= npools) {
+      snprintf(buf, sizeof buf, "request %d: pool index %d out of range", i, r.pool);
+      return fail(VC_EINVAL, buf);
+    }
+    if (r.slot < 0 || r.ctx_len < 0 || r.page_row < 0 || r.q0 < 0 || r.rows < 1 ||
+        r.q0 + r.rows > s->max_rows) {
+      snprintf(buf, sizeof buf, "request %d: bad slot/ctx_len/page_row/q0/rows", i);
+      return fail(VC_EINVAL, buf);
+    }
+    if (r.kind == VC_DRAFT && r.rows * G > 16) {
+      snprintf(buf, sizeof buf, "request %d: a draft step needs rows * G <= 16", i);
+      return fail(VC_EINVAL, buf);
+    }
+    const vc_pool& p = pools[r.pool];
+    if (!pool_used[r.pool]) {
+      rc = check_pool(&p, D, "attention");
+      if (rc) return rc;
+      pool_used[r.pool] = 1;
+    }
+    if (r.kind == VC_VERIFY && p.bits != 16) {
+      snprintf(buf, sizeof buf, "request %d: the verify pass reads a bf16 pool", i);
+      return fail(VC_EINVAL, buf);
+    }
+    const int pages = (r.ctx_len + kBlock - 1) / kBlock;
+    if (pages > p.max_pages) {
+      snprintf(buf, sizeof buf, "request %d: %d pages exceed the page table width %d", i, pages,
+               p.max_pages);
+      return fail(VC_EINVAL, buf);
+    }
+    ReqDev& d = args->reqs[i];
+    d.slot = r.slot;
+    d.pool = r.pool;
+    d.ctx_len = r.ctx_len;
+    d.page_row = r.page_row;
+    d.q0 = r.q0;
+    d.rows = r.rows;
+    d.kind = r.kind;
+    d.chunk_pages = chunk;
+    d.nsplit = pages > 0 ? (pages + chunk - 1) / chunk : 1;
+    d.nrg = r.kind == VC_VERIFY ? (r.rows * G + 127) / 128 : 1;
+    d.item_base = (int32_t)items;
+    items += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * d.nrg;
+    if (d.nsplit > 1) {
+      d.part_base = part;
+      part += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * r.rows * G * (D + 4);
+      plan->any_split = 1;
+    } else {
+      d.part_base = -1;
+    }
+  }
+  if (items > (1LL << 30)) return fail(VC_EINVAL, "too many work items");
+  args->L = s->num_layers;
+  args->Hq = s->num_q_heads;
+  args->Hkv = s->num_kv_heads;
+  args->G = G;
+  args->xmax = s->max_rows;
+  args->nreq = nreq;
+  args->nitems = (int)items;
+  args->nitems_pad = (int)((items + 7) / 8 * 8);
+  args->scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  plan->nitems = (int)items;
+  plan->part_floats = part;
+  plan->head_dim = D;
+  return VC_OK;
+}
+
+static int attn_common(const vc_shape* s, int nreq, const vc_req* reqs, const void* q,
+                       const void* blk_k, const void* blk_v, int npools, const vc_pool* pools,
+                       float* out, void* ws, size_t ws_bytes, int split_pages, void* stream) {
+  AttnArgs args;
+  Plan plan;
+  int rc = plan_attn(s, nreq, reqs, npools, pools, split_pages, &args, &plan);
+  if (rc) return rc;
+  if (nreq == 0 || plan.nitems == 0) return VC_OK;
+  if (!q || !blk_k || !blk_v || !out) return fail(VC_EINVAL, "q, blk_k, blk_v and out must be set");
+  const size_t need = (size_t)plan.part_floats * sizeof(float);
+  if (need > 0 && (!ws || ws_bytes < need)) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    return fail(VC_ENOSPACE, buf);
+  }
+  args.q = static_cast<const uint16_t*>(q);
+  args.blk_k = static_cast<const uint16_t*>(blk_k);
+  args.blk_v = static_cast<const uint16_t*>(blk_v);
+  args.out = out;
+  args.part = static_cast<float*>(ws);
+  return launch_attn(args, plan, s->head_dim, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" {
+
+const char* vc_last_error(void) { return g_last_error.c_str(); }
+
+const char* vc_version(void) { return "vc 0.1 gfx950"; }
+
+size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req* reqs,
+                              int split_pages) {
+  // pools are not needed for sizing: validate with a permissive dummy pool per index
+  if (check_shape(shape)) return 0;
+  if (num_reqs <= 0 || num_reqs > VC_MAX_REQS || !reqs) return 0;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const int chunk = split_pages > 0 ? split_pages : auto_chunk(shape, num_reqs, reqs);
+  if (chunk <= 0) return 0;
+  size_t floats = 0;
+  for (int i = 0; i < num_reqs; ++i) {
+    const int pages = (reqs[i].ctx_len + kBlock - 1) / kBlock;
+    const int nsplit = pages > 0 ? (pages + chunk - 1) / chunk : 1;
+    if (nsplit > 1)
+      floats += (size_t)shape->num_layers * shape->num_kv_heads * nsplit * reqs[i].rows * G *
+                (shape->head_dim + 4);
+  }
+  return floats * sizeof(float);
+}
+
+int vc_verify_attn(const vc_shape* shape, int num_reqs, const vc_req* reqs, const void* q,
+                   const void* blk_k, const void* blk_v, const vc_pool* full, float* out,
+                   void* workspace, size_t workspace_bytes, int split_pages, void* stream) {
+  set_error("");
+  if (num_reqs < 0 || num_reqs > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 64]");
+  if (num_reqs > 0 && !reqs) return fail(VC_EINVAL, "reqs is NULL");
+  if (!full) return fail(VC_EINVAL, "full pool is NULL");
+  vc_req rr[VC_MAX_REQS];
+  for (int i = 0; i < num_reqs; ++i) {
+    rr[i] = reqs[i];
+    rr[i].pool = 0;
+    rr[i].kind = VC_VERIFY;
+  }
+  return attn_common(shape, num_reqs, rr, q, blk_k, blk_v, 1, full, out, workspace,
+                     workspace_bytes, split_pages, stream);
+}
+
+int vc_draft_attn(const vc_shape* shape, int num_reqs, const vc_req* reqs, const void* q,
+                  const void* blk_k, const void* blk_v, const vc_pool* comp, float* out,
+                  void* workspace, size_t workspace_bytes, int split_pages, void* stream) {
+  set_error("");
+  if (num_reqs < 0 || num_reqs > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 64]");
+  if (num_reqs > 0 && !reqs) return fail(VC_EINVAL, "reqs is NULL");
+  if (!comp) return fail(VC_EINVAL, "compressed pool is NULL");
+  vc_req rr[VC_MAX_REQS];
+  for (int i = 0; i < num_reqs; ++i) {
+    rr[i] = reqs[i];
+    rr[i].pool = 0;
+    rr[i].kind = VC_DRAFT;
+  }
+  return attn_common(shape, num_reqs, rr, q, blk_k, blk_v, 1, comp, out, workspace,
+                     workspace_bytes, split_pages, stream);
+}
+
+int vc_attn_mixed(const vc_shape* shape, int num_reqs, const vc_req* reqs, const void* q,
+                  const void* blk_k, const void* blk_v, int num_pools, const vc_pool* pools,
+                  float* out, void* workspace, size_t workspace_bytes, int split_pages,
+                  void* stream) {
+  set_error("");
+  if (!pools) return fail(VC_EINVAL, "pools is NULL");
+  return attn_common(shape, num_reqs, reqs, q, blk_k, blk_v, num_pools, pools, out, workspace,
+                     workspace_bytes, split_pages, stream);
+}
+
+int vc_stage_kv(void* dst_device, const void* src_pinned_host, size_t bytes, void* side_stream,
+                void* event) {
+  set_error("");
+  if (bytes == 0) return VC_OK;
+  if (!dst_device || !src_pinned_host) return fail(VC_EINVAL, "dst and src must be set");
+  hipStream_t st = static_cast<hipStream_t>(side_stream);
+  int rc = hip_check(hipMemcpyAsync(dst_device, src_pinned_host, bytes, hipMemcpyHostToDevice, st),
+                     "hipMemcpyAsync");
+  if (rc) return rc;
+  if (event) rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(event), st), "hipEventRecord");
+  return rc;
+}
+
+}  // extern "C"

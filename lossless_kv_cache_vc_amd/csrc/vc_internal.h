@@ -1,0 +1,80 @@
+// Internal declarations shared by the library's translation units (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/vc.h"
+
+namespace vc {
+
+// ---------------------------------------------------------------- error reporting (host)
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+int hip_check(hipError_t e, const char* what);
+
+// ---------------------------------------------------------------- device vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = VC_BLOCK_TOKENS;
+constexpr int kMaxReqs = VC_MAX_REQS;
+
+// Pool descriptor as the kernels see it (passed by value in kernel arguments).
+struct PoolDev {
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* ksz;
+  const uint8_t* vsz;
+  const int32_t* page_table;
+  int64_t nblk;
+  int32_t max_pages;
+  int32_t bits;
+};
+
+// Per-request launch plan (host computed, passed by value).
+struct ReqDev {
+  int32_t slot, pool, ctx_len, page_row, q0, rows, kind;
+  int32_t item_base;    // first work item of this request
+  int32_t nsplit;       // context splits per (layer, kv head)
+  int32_t nrg;          // row groups per (layer, kv head, split) (verify); 1 for draft
+  int32_t chunk_pages;  // context pages per split
+  int64_t part_base;    // float offset of this request's partials in the workspace (-1: none)
+};
+
+constexpr int kMaxPools = 4;
+
+struct AttnArgs {
+  PoolDev pools[kMaxPools];
+  const uint16_t* q;
+  const uint16_t* blk_k;
+  const uint16_t* blk_v;
+  float* out;
+  float* part;
+  int32_t L, Hq, Hkv, G, xmax, nreq, nitems, nitems_pad;
+  float scale_log2;  // log2(e) / sqrt(d)
+  ReqDev reqs[kMaxReqs];
+};
+
+static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit 4 KiB");
+
+// Plan an attention launch: fills reqs/nitems and returns workspace floats needed.
+struct Plan {
+  int nitems = 0;
+  int64_t part_floats = 0;
+  int any_split = 0;
+  int head_dim = 0;
+};
+int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const vc_pool* pools,
+              int split_pages, AttnArgs* args, Plan* plan);
+
+int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_t stream);
+
+}  // namespace vc

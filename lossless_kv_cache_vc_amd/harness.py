@@ -1,0 +1,311 @@
+"""Device-side synthetic workload and one draft–verify round through the C ABI.
+
+Inputs are drawn on the GPU by the seeded generator (``vcsynth``), packed into paged pools,
+compressed by the library's own kernels, and run through draft attention (x single-query steps
+over the compressed cache), verify attention (x causal rows over the full cache), the LM-head
+stand-in and the greedy accept — the per-request cycle of the VeriCache review
+(§Draft–Verify Pipeline).  PyTorch only allocates memory and provides the stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import torch
+
+from vcsynth import configs as C
+from vcsynth import gpu as sg
+from vcsynth import rng
+from vcsynth.configs import NPOS, XMAX
+
+from . import vc
+
+BF16 = torch.bfloat16
+
+
+def round16(x: int) -> int:
+    return (x + 15) // 16 * 16
+
+
+def _pages(n: int) -> int:
+    return (n + 15) // 16
+
+
+@dataclass
+class Timing:
+    ms: Dict[str, float] = field(default_factory=dict)
+
+
+class Workload:
+    """All device tensors of one configuration plus the launch lists of a round."""
+
+    def __init__(self, cfg: C.Config, device: str = "cuda:0", build_compressed: bool = True,
+                 keep_dense_scores: bool = False):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        B, L, Hq, Hkv, d = cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.d
+        self.xmax = round16(max(r.x for r in cfg.reqs))
+        assert self.xmax <= XMAX
+        self.shape = vc.shape(L, Hq, Hkv, d, self.xmax)
+        seed = cfg.seed
+        dev = self.dev
+        with torch.cuda.device(dev):
+            xm, P = self.xmax, self.xmax // 16
+            self.q = torch.empty((B, L, xm, Hq, d), dtype=BF16, device=dev)
+            sg.fill_normal_bf16(self.q, [L * XMAX * Hq * d, XMAX * Hq * d, Hq * d, d, 1], 0, seed,
+                                rng.STREAM_Q)
+            bs = [L * XMAX * Hkv * d, XMAX * Hkv * d, d, 16 * Hkv * d]
+            self.blk_k = torch.empty((B, L, Hkv, P, 16, d), dtype=BF16, device=dev)
+            sg.fill_normal_bf16(self.blk_k, bs + [Hkv * d, 1], 0, seed, rng.STREAM_KBLK)
+            self.blk_v = torch.empty((B, L, Hkv, P, d, 16), dtype=BF16, device=dev)
+            sg.fill_normal_bf16(self.blk_v, bs + [1, Hkv * d], 0, seed, rng.STREAM_VBLK)
+            self.w_u = torch.empty((cfg.wu_width, cfg.vocab), dtype=BF16, device=dev)
+            sg.fill_normal_bf16(self.w_u, [cfg.vocab, 1], 0, seed, rng.STREAM_WU, sigma=cfg.wu_sigma)
+
+            self.lens = [r.ctx_len for r in cfg.reqs]
+            self.full = self._bf16_pool(self.lens, salt=0)
+            self._fill_full()
+
+            self.out_v = torch.zeros((B, L, xm, Hq, d), dtype=torch.float32, device=dev)
+            self.out_d = torch.zeros((B, L, xm, Hq, d), dtype=torch.float32, device=dev)
+            self.drop_pool: Optional[vc.PagedPool] = None
+            self.kivi_pool: Optional[vc.PagedPool] = None
+            self.kept: Optional[torch.Tensor] = None
+            if build_compressed:
+                self._build_compressed(keep_dense_scores)
+            self.workspace = self._workspace()
+
+    # ---------------------------------------------------------------- pools
+    def _bf16_pool(self, lens: List[int], salt: int) -> vc.PagedPool:
+        cfg = self.cfg
+        pt, nblk = C.page_tables(cfg.seed, lens, salt=salt)
+        shape = (cfg.L, nblk, cfg.Hkv, 16, cfg.d)
+        k = torch.empty(shape, dtype=BF16, device=self.dev)
+        v = torch.empty(shape, dtype=BF16, device=self.dev)
+        return vc.PagedPool(16, torch.from_numpy(pt).to(self.dev), k, v, nblk)
+
+    def _kivi_pool(self, lens: List[int], bits: int, salt: int) -> vc.PagedPool:
+        cfg = self.cfg
+        pt, nblk = C.page_tables(cfg.seed, lens, salt=salt)
+        d, L, Hkv = cfg.d, cfg.L, cfg.Hkv
+        k = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
+        v = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
+        ksz = torch.empty((L, nblk, Hkv, d, 2), dtype=torch.int16, device=self.dev)
+        vsz = torch.empty((L, nblk, Hkv, d // 32, 16, 2), dtype=torch.int16, device=self.dev)
+        return vc.PagedPool(bits, torch.from_numpy(pt).to(self.dev), k, v, nblk, ksz, vsz)
+
+    @staticmethod
+    def _row(pool: vc.PagedPool, r: int) -> vc.PagedPool:
+        return vc.PagedPool(pool.bits, pool.page_table[r:r + 1], pool.k, pool.v, pool.num_blocks,
+                            pool.k_sz, pool.v_sz)
+
+    def _fill_full(self):
+        cfg = self.cfg
+        Hkv, d, L = cfg.Hkv, cfg.d, cfg.L
+        for r, n in enumerate(self.lens):
+            if n == 0:
+                continue
+            src = torch.empty((1, Hkv, n, d), dtype=BF16, device=self.dev)
+            row = self._row(self.full, r)
+            for l in range(L):
+                base = ((r * L + l) * Hkv) * NPOS * d
+                for which, stream in ((0, rng.STREAM_KCTX), (1, rng.STREAM_VCTX)):
+                    sg.fill_normal_bf16(src, [0, NPOS * d, d, 1], base, cfg.seed, stream)
+                    vc.pack_bf16(self.shape, [n], l, src, n, row, which)
+            del src
+
+    def comp_len(self, r: int) -> int:
+        return self.cfg.reqs[r].kept
+
+    def drafts(self, r: int) -> bool:
+        req = self.cfg.reqs[r]
+        return req.kind != C.KIND_VERIFY
+
+    def _build_compressed(self, keep_scores: bool):
+        cfg = self.cfg
+        B, L, Hkv = cfg.B, cfg.L, cfg.Hkv
+        reqs = cfg.reqs
+        drop_lens = [r.kept if (self.drafts(i) and r.comp in (C.COMP_DROP, C.COMP_DROP_KIVI4)) else 0
+                     for i, r in enumerate(reqs)]
+        kivi_lens = [r.kept if (self.drafts(i) and r.comp in (C.COMP_KIVI2, C.COMP_DROP_KIVI4)) else 0
+                     for i, r in enumerate(reqs)]
+        nmax = max(self.lens)
+        if any(drop_lens):
+            scores = torch.empty((B, L, Hkv, nmax), dtype=torch.int32, device=self.dev)
+            sg.fill_u32(scores, [L * Hkv * NPOS, Hkv * NPOS, NPOS, 1], 0, cfg.seed, rng.STREAM_SCORE)
+            kmax = max(drop_lens)
+            self.kept = torch.empty((B, L, Hkv, kmax), dtype=torch.int32, device=self.dev)
+            sel_lens = [n if k else 0 for n, k in zip(self.lens, drop_lens)]
+            vc.select_kept(self.shape, sel_lens, [r.recent for r in reqs], [r.top for r in reqs],
+                           scores, nmax, self.kept, kmax)
+            if keep_scores:
+                self.scores = scores
+            else:
+                del scores
+        bf16_drop = [k if reqs[i].comp == C.COMP_DROP else 0 for i, k in enumerate(drop_lens)]
+        if any(bf16_drop):
+            self.drop_pool = self._bf16_pool(bf16_drop, salt=1)
+            vc.compress(self.shape, bf16_drop, self.full, self.kept, self.kept.shape[-1], self.drop_pool)
+        if any(kivi_lens):
+            bits = {C.COMP_KIVI2: 2, C.COMP_DROP_KIVI4: 4}
+            kinds = {reqs[i].comp for i, k in enumerate(kivi_lens) if k}
+            assert len(kinds) == 1, "one KIVI bit width per workload"
+            b = bits[kinds.pop()]
+            self.kivi_pool = self._kivi_pool(kivi_lens, b, salt=2)
+            with_kept = [k if reqs[i].comp == C.COMP_DROP_KIVI4 else 0 for i, k in enumerate(kivi_lens)]
+            plain = [k if reqs[i].comp == C.COMP_KIVI2 else 0 for i, k in enumerate(kivi_lens)]
+            if any(with_kept):
+                vc.compress(self.shape, with_kept, self.full, self.kept, self.kept.shape[-1], self.kivi_pool)
+            if any(plain):
+                vc.compress(self.shape, plain, self.full, None, 0, self.kivi_pool)
+
+    def draft_pool_of(self, r: int) -> vc.PagedPool:
+        comp = self.cfg.reqs[r].comp
+        return self.drop_pool if comp == C.COMP_DROP else self.kivi_pool
+
+    # ---------------------------------------------------------------- launch lists
+    def verify_reqs(self) -> List[vc.Req]:
+        return [vc.Req(r, 0, n, r, 0, self.cfg.reqs[r].x, vc.VC_VERIFY)
+                for r, n in enumerate(self.lens) if self.cfg.reqs[r].kind in (None, C.KIND_VERIFY)]
+
+    def draft_reqs(self, step: int) -> List[vc.Req]:
+        return [vc.Req(r, 0, self.comp_len(r), r, step, 1, vc.VC_DRAFT)
+                for r in range(self.cfg.B) if step < self.cfg.reqs[r].x]
+
+    def mixed_reqs(self) -> List[vc.Req]:
+        """Ragged batch: pools 0 = full, 1 = bf16 drop, 2 = KIVI."""
+        out = []
+        for r, req in enumerate(self.cfg.reqs):
+            if req.kind == C.KIND_DRAFT:
+                pool = 1 if req.comp == C.COMP_DROP else 2
+                out.append(vc.Req(r, pool, req.kept, r, req.step, 1, vc.VC_DRAFT))
+            else:
+                out.append(vc.Req(r, 0, req.ctx_len, r, 0, req.x, vc.VC_VERIFY))
+        return out
+
+    def mixed_pools(self) -> List[vc.PagedPool]:
+        dummy = self.full
+        return [self.full, self.drop_pool or dummy, self.kivi_pool or dummy]
+
+    def _workspace(self) -> Optional[torch.Tensor]:
+        need = 0
+        if self.cfg.mixed:
+            need = vc.attn_workspace_size(self.shape, self.mixed_reqs())
+        else:
+            need = vc.attn_workspace_size(self.shape, self.verify_reqs())
+            if self.drop_pool is not None or self.kivi_pool is not None:
+                for i in range(self.xmax):
+                    rq = self.draft_reqs(i)
+                    if rq:
+                        need = max(need, vc.attn_workspace_size(self.shape, rq))
+        if need == 0:
+            return None
+        return torch.empty(need // 4 + 1, dtype=torch.float32, device=self.dev)
+
+    # ---------------------------------------------------------------- passes
+    def run_verify(self, split_pages: int = 0, out: Optional[torch.Tensor] = None):
+        vc.verify_attn(self.shape, self.verify_reqs(), self.q, self.blk_k, self.blk_v, self.full,
+                       self.out_v if out is None else out, self.workspace_for(split_pages, "v"), split_pages)
+
+    def run_draft(self, step: int, split_pages: int = 0, out: Optional[torch.Tensor] = None):
+        rq = self.draft_reqs(step)
+        if not rq:
+            return
+        pool = self.drop_pool if self.drop_pool is not None else self.kivi_pool
+        vc.draft_attn(self.shape, rq, self.q, self.blk_k, self.blk_v, pool,
+                      self.out_d if out is None else out, self.workspace_for(split_pages, "d", step),
+                      split_pages)
+
+    def run_mixed(self, split_pages: int = 0, out: Optional[torch.Tensor] = None):
+        vc.attn_mixed(self.shape, self.mixed_reqs(), self.q, self.blk_k, self.blk_v, self.mixed_pools(),
+                      self.out_v if out is None else out, self.workspace_for(split_pages, "m"), split_pages)
+
+    def workspace_for(self, split_pages: int, which: str, step: int = 0):
+        if split_pages == 0:
+            return self.workspace
+        rq = {"v": self.verify_reqs, "m": self.mixed_reqs}.get(which)
+        reqs = rq() if rq else self.draft_reqs(step)
+        need = vc.attn_workspace_size(self.shape, reqs, split_pages)
+        if need == 0:
+            return None
+        key = ("ws", split_pages, which, step)
+        cache = getattr(self, "_ws_cache", {})
+        t = cache.get(key)
+        if t is None or t.numel() * 4 < need:
+            t = torch.empty(need // 4 + 1, dtype=torch.float32, device=self.dev)
+            cache[key] = t
+            self._ws_cache = cache
+        return t
+
+    def logits_and_accept(self):
+        cfg = self.cfg
+        B, L, xm, V = cfg.B, cfg.L, self.xmax, cfg.vocab
+        width = cfg.Hq * cfg.d
+        rows = B * L * xm
+        if not hasattr(self, "z_v"):
+            self.z_v = torch.empty((rows, V), dtype=torch.float32, device=self.dev)
+            self.z_d = torch.empty((rows, V), dtype=torch.float32, device=self.dev)
+            xs = torch.tensor([cfg.reqs[r].x for r in range(B) for _ in range(L)], dtype=torch.int32)
+            self.x_dev = xs.to(self.dev)
+            self.tok_d = torch.empty((B * L, xm), dtype=torch.int32, device=self.dev)
+            self.tok_v = torch.empty((B * L, xm), dtype=torch.int32, device=self.dev)
+            self.acc_len = torch.empty(B * L, dtype=torch.int32, device=self.dev)
+            self.next_tok = torch.empty(B * L, dtype=torch.int32, device=self.dev)
+        vc.logits(rows, width, V, self.out_v, width, self.w_u, self.z_v)
+        vc.logits(rows, width, V, self.out_d, width, self.w_u, self.z_d)
+        vc.accept(B * L, xm, xm, V, self.x_dev, self.x_dev, self.z_d, self.z_v, self.tok_d, self.tok_v,
+                  self.acc_len, self.next_tok)
+
+    def run_round(self):
+        """x draft steps, the verify pass, logits of both, accept."""
+        for i in range(max(r.x for r in self.cfg.reqs)):
+            self.run_draft(i)
+        self.run_verify()
+        self.logits_and_accept()
+
+    # ---------------------------------------------------------------- algorithmic bytes
+    def verify_bytes(self) -> int:
+        """Bytes the verify pass must move: context K/V, drafted-block K/V, Q, O, page tables."""
+        cfg = self.cfg
+        tot = 0
+        for r in self.verify_reqs():
+            x = r.rows
+            tot += cfg.L * cfg.Hkv * (r.ctx_len * cfg.d * 2 * 2 + x * cfg.d * 2 * 2)
+            tot += cfg.L * x * cfg.Hq * cfg.d * (2 + 4)
+            tot += _pages(r.ctx_len) * 4
+        return tot
+
+    def draft_bytes(self, step: int) -> int:
+        """Bytes one draft step must move: the compressed cache, visible drafted rows, q, o."""
+        cfg = self.cfg
+        tot = 0
+        for r in self.draft_reqs(step):
+            tot += cfg.L * cfg.Hkv * self.comp_token_bytes(r.slot) * r.ctx_len
+            tot += cfg.L * cfg.Hkv * (step + 1) * cfg.d * 2 * 2
+            tot += cfg.L * cfg.Hq * cfg.d * (2 + 4)
+            tot += _pages(r.ctx_len) * 4
+        return tot
+
+    def comp_token_bytes(self, r: int) -> float:
+        """Bytes per stored token and kv head of request r's drafting cache."""
+        d = self.cfg.d
+        req = self.cfg.reqs[r]
+        if req.comp == C.COMP_DROP:
+            return 2 * d * 2
+        b = req.bits
+        # K and V codes, value (scale, zero) per 32 channels, key (scale, zero) per 32 tokens
+        return 2 * d * b / 8 + (d // 32) * 4 + d * 4 / 32
+
+    def mixed_bytes(self) -> int:
+        cfg = self.cfg
+        tot = 0
+        for r in self.mixed_reqs():
+            if r.kind == vc.VC_VERIFY:
+                tot += cfg.L * cfg.Hkv * (r.ctx_len + r.rows) * cfg.d * 4
+                tot += cfg.L * r.rows * cfg.Hq * cfg.d * 6
+            else:
+                tot += int(cfg.L * cfg.Hkv * (self.comp_token_bytes(r.slot) * r.ctx_len +
+                                              (r.q0 + 1) * cfg.d * 4))
+                tot += cfg.L * cfg.Hq * cfg.d * 6
+            tot += _pages(r.ctx_len) * 4
+        return tot

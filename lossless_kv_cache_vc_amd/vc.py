@@ -1,0 +1,208 @@
+"""ctypes binding of the C ABI in include/vc.h (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU and passes their device
+pointers; all arithmetic happens in the HIP kernels of libvc.so.  If the library is not built
+the binding raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBVC_PATH = os.path.join(PKG, "libvc.so")
+
+VC_OK, VC_EINVAL, VC_ENOSPACE, VC_EHIP, VC_EUNSUPPORTED = 0, -1, -2, -3, -4
+VC_VERIFY, VC_DRAFT = 0, 1
+BLOCK = 16
+MAX_REQS = 64
+MAX_ROWS = 64
+
+# every symbol include/vc.h declares
+EXPORTS = (
+    "vc_attn_workspace_size", "vc_verify_attn", "vc_draft_attn", "vc_attn_mixed", "vc_accept",
+    "vc_logits", "vc_pack_bf16", "vc_select_kept", "vc_compress", "vc_stage_kv",
+    "vc_last_error", "vc_version",
+)
+
+
+class VCError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"vc error {code}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32)]
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("page_table", ctypes.c_void_p),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_sz", ctypes.c_void_p), ("v_sz", ctypes.c_void_p)]
+
+
+class Req(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_int32), ("pool", ctypes.c_int32), ("ctx_len", ctypes.c_int32),
+                ("page_row", ctypes.c_int32), ("q0", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("kind", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libvc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBVC_PATH):
+            raise ImportError(f"{LIBVC_PATH} is missing: build it with "
+                              "`python -m lossless_kv_cache_vc_amd.build`")
+        L = ctypes.CDLL(LIBVC_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.vc_last_error.restype = ctypes.c_char_p
+        L.vc_version.restype = ctypes.c_char_p
+        L.vc_attn_workspace_size.restype = sz
+        L.vc_attn_workspace_size.argtypes = [P(Shape), i32, P(Req), i32]
+        attn = [P(Shape), i32, P(Req), vp, vp, vp, P(Pool), vp, vp, sz, i32, vp]
+        L.vc_verify_attn.argtypes = attn
+        L.vc_draft_attn.argtypes = attn
+        L.vc_attn_mixed.argtypes = [P(Shape), i32, P(Req), vp, vp, vp, i32, P(Pool), vp, vp, sz, i32, vp]
+        L.vc_accept.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.vc_logits.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp]
+        L.vc_pack_bf16.argtypes = [P(Shape), i32, vp, i32, vp, i64, P(Pool), i32, vp]
+        L.vc_select_kept.argtypes = [P(Shape), i32, vp, vp, vp, vp, i64, vp, i64, vp]
+        L.vc_compress.argtypes = [P(Shape), i32, vp, P(Pool), vp, i64, P(Pool), vp]
+        L.vc_stage_kv.argtypes = [vp, vp, sz, vp, vp]
+        for name in EXPORTS:
+            if name not in ("vc_last_error", "vc_version", "vc_attn_workspace_size"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != VC_OK:
+        raise VCError(rc, lib().vc_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _i32_array(vals: Sequence[int]):
+    return (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+
+
+@dataclass
+class PagedPool:
+    """A paged KV pool: device tensors plus the page table (see vc_pool in include/vc.h)."""
+    bits: int
+    page_table: "object"       # int32 [rows][max_pages] (device)
+    k: "object"
+    v: "object"
+    num_blocks: int
+    k_sz: "object" = None
+    v_sz: "object" = None
+
+    def desc(self) -> Pool:
+        return Pool(self.bits, int(self.page_table.shape[1]), int(self.num_blocks),
+                    _ptr(self.page_table), _ptr(self.k), _ptr(self.v), _ptr(self.k_sz),
+                    _ptr(self.v_sz))
+
+
+def shape(L: int, Hq: int, Hkv: int, d: int, max_rows: int) -> Shape:
+    return Shape(L, Hq, Hkv, d, max_rows)
+
+
+def reqs_array(reqs: Sequence[Req]):
+    arr = (Req * max(1, len(reqs)))()
+    for i, r in enumerate(reqs):
+        arr[i] = r
+    return arr
+
+
+def attn_workspace_size(shp: Shape, reqs: Sequence[Req], split_pages: int = 0) -> int:
+    arr = reqs_array(reqs)
+    return int(lib().vc_attn_workspace_size(ctypes.byref(shp), len(reqs), arr, split_pages))
+
+
+def verify_attn(shp, reqs, q, blk_k, blk_v, full: PagedPool, out, workspace=None, split_pages=0,
+                stream=None):
+    arr = reqs_array(reqs)
+    pd = full.desc()
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vc_verify_attn(ctypes.byref(shp), len(reqs), arr, _ptr(q), _ptr(blk_k), _ptr(blk_v),
+                                ctypes.byref(pd), _ptr(out), _ptr(workspace), ws, split_pages,
+                                _stream(stream)))
+
+
+def draft_attn(shp, reqs, q, blk_k, blk_v, comp: PagedPool, out, workspace=None, split_pages=0,
+               stream=None):
+    arr = reqs_array(reqs)
+    pd = comp.desc()
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vc_draft_attn(ctypes.byref(shp), len(reqs), arr, _ptr(q), _ptr(blk_k), _ptr(blk_v),
+                               ctypes.byref(pd), _ptr(out), _ptr(workspace), ws, split_pages,
+                               _stream(stream)))
+
+
+def attn_mixed(shp, reqs, q, blk_k, blk_v, pools: Sequence[PagedPool], out, workspace=None,
+               split_pages=0, stream=None):
+    arr = reqs_array(reqs)
+    parr = (Pool * len(pools))(*[p.desc() for p in pools])
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vc_attn_mixed(ctypes.byref(shp), len(reqs), arr, _ptr(q), _ptr(blk_k), _ptr(blk_v),
+                               len(pools), parr, _ptr(out), _ptr(workspace), ws, split_pages,
+                               _stream(stream)))
+
+
+def accept(n_inst, max_x, max_xv, vocab, x, xv, draft_logits, verify_logits, draft_tok, verify_tok,
+           accept_len, next_tok, stream=None):
+    _check(lib().vc_accept(n_inst, max_x, max_xv, vocab, _ptr(x), _ptr(xv), _ptr(draft_logits),
+                           _ptr(verify_logits), _ptr(draft_tok), _ptr(verify_tok), _ptr(accept_len),
+                           _ptr(next_tok), _stream(stream)))
+
+
+def logits(rows, width, vocab, o, ld_o, w_u, z, stream=None):
+    _check(lib().vc_logits(rows, width, vocab, _ptr(o), ld_o, _ptr(w_u), _ptr(z), _stream(stream)))
+
+
+def pack_bf16(shp, lens, layer, src, src_rows, pool: PagedPool, which, stream=None):
+    pd = pool.desc()
+    _check(lib().vc_pack_bf16(ctypes.byref(shp), len(lens), _i32_array(lens), layer, _ptr(src),
+                              src_rows, ctypes.byref(pd), which, _stream(stream)))
+
+
+def select_kept(shp, lens, recent, top, scores, score_stride, kept, kept_stride, stream=None):
+    _check(lib().vc_select_kept(ctypes.byref(shp), len(lens), _i32_array(lens), _i32_array(recent),
+                                _i32_array(top), _ptr(scores), score_stride, _ptr(kept), kept_stride,
+                                _stream(stream)))
+
+
+def compress(shp, comp_lens, src: PagedPool, kept, kept_stride, dst: PagedPool, stream=None):
+    sd, dd = src.desc(), dst.desc()
+    _check(lib().vc_compress(ctypes.byref(shp), len(comp_lens), _i32_array(comp_lens), ctypes.byref(sd),
+                             _ptr(kept), kept_stride, ctypes.byref(dd), _stream(stream)))
+
+
+def stage_kv(dst, src_pinned, nbytes, side_stream, event=None):
+    ev = None if event is None else event.cuda_event
+    _check(lib().vc_stage_kv(_ptr(dst), _ptr(src_pinned), nbytes, _stream(side_stream), ev))
+
+
+def version() -> str:
+    return lib().vc_version().decode()

@@ -1,0 +1,111 @@
+"""Shared helpers of the GPU tests: reading pool pages back and comparing with the oracle."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+from vcsynth import configs as C
+
+TOL_CONTRACT = 5e-3   # max-abs bound on attention outputs (the contract)
+
+
+def tight_tol(n_keys: int, kivi: bool = False) -> float:
+    """Internal gate derived from the kernel's arithmetic.  The value product multiplies softmax
+    weights rounded to bf16 (relative error uniform within +-2^-8, standard deviation about
+    2^-9), so with N(0,1) values an output element carries an error of about
+    2^-9 * sqrt(e / n_keys) (softmax over N(0,1) scores has about n_keys / e effective keys).
+    The gate allows 12 of those plus 1e-4: ~3e-4 at 32K keys, ~4e-3 at 100 keys, never above
+    the contract.  The KIVI path rounds its dequantised keys, values and weights to fp16
+    (2^-11) instead, which keeps it inside the same gate."""
+    base = 2.0 ** -9 * np.sqrt(np.e / max(1, n_keys))
+    return float(min(TOL_CONTRACT, 12 * base + 1e-4))
+
+
+ERRLOG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                      "parity_errors.txt")
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+
+
+def bf16_tensor_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def unpack_codes(words: np.ndarray, bits: int, count: int) -> np.ndarray:
+    """Codes 0..count-1 of a little-endian uint32 word stream, packed as documented in vc.h:
+    code u of a word sits at bit (u%2)*16 + bits*(u/2)."""
+    per = 32 // bits
+    u = np.arange(count)
+    w = words[..., u // per]
+    uu = u % per
+    shift = (uu % 2) * 16 + bits * (uu // 2)
+    return ((w >> shift.astype(np.uint32)) & np.uint32((1 << bits) - 1)).astype(np.uint8)
+
+
+def pool_tokens_bf16(pool, layer: int, r: int, g: int, n: int, d: int):
+    """Read tokens [0, n) of (r, layer, g) back from a bf16 pool: (K [n][d], V [n][d]) float64."""
+    pt = pool.page_table[r].cpu().numpy()
+    npg = (n + 15) // 16
+    ks, vs = [], []
+    for p in range(npg):
+        b = int(pt[p])
+        ks.append(pool.k[layer, b, g].float().cpu().numpy())          # [16][d]
+        vs.append(pool.v[layer, b, g].reshape(d, 16).float().cpu().numpy().T)  # [d][16] -> [16][d]
+    k = np.concatenate(ks)[:n].astype(np.float64)
+    v = np.concatenate(vs)[:n].astype(np.float64)
+    return k, v
+
+
+def pool_kivi(pool, layer: int, r: int, g: int, T: int, d: int):
+    """Codes and (scale, zero) of (r, layer, g) from a KIVI pool, in the oracle's logical layout:
+    kcodes [T][d], kscale/kzero [ceil(T/32)][d], vcodes [T][d], vscale/vzero [T][d/32]."""
+    bits = pool.bits
+    pt = pool.page_table[r].cpu().numpy()
+    npg = (T + 15) // 16
+    kc, vc_, vs, vz = [], [], [], []
+    ks, kz = [], []
+    for p in range(npg):
+        b = int(pt[p])
+        kw = pool.k[layer, b, g].cpu().numpy().view(np.uint32).reshape(16, d * bits // 32)
+        kc.append(unpack_codes(kw, bits, d))                            # [16][d]
+        vw = pool.v[layer, b, g].cpu().numpy().view(np.uint32).reshape(d, 16 * bits // 32)
+        vc_.append(unpack_codes(vw, bits, 16).T)                        # [16][d]
+        vsz = pool.v_sz[layer, b, g].cpu().numpy().view(np.float16)     # [d/32][16][2]
+        vs.append(vsz[:, :, 0].T)
+        vz.append(vsz[:, :, 1].T)
+        if p % 2 == 0:
+            ksz = pool.k_sz[layer, b, g].cpu().numpy().view(np.float16)  # [d][2]
+            ks.append(ksz[:, 0])
+            kz.append(ksz[:, 1])
+    return dict(kcodes=np.concatenate(kc)[:T], vcodes=np.concatenate(vc_)[:T],
+                kscale=np.stack(ks), kzero=np.stack(kz),
+                vscale=np.concatenate(vs)[:T], vzero=np.concatenate(vz)[:T])
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, tol: float, what: str):
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    if os.path.isdir(os.path.dirname(ERRLOG)):
+        with open(ERRLOG, "a") as f:
+            f.write(f"{what}\tmax_abs={err:.3e}\ttol={tol:.1e}\n")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err <= TOL_CONTRACT, f"{what}: max-abs error {err:.3e} > contract {TOL_CONTRACT:.0e}"
+    assert err <= tol, f"{what}: max-abs error {err:.3e} > derived gate {tol:.1e}"
+    return err
+
+
+def tokens_match(tok_gpu, tok_or, gap_or, z_or, tie=1e-3):
+    """Argmax tokens must be equal except at flagged near-tie rows, where the GPU's token must lie
+    in the oracle's tie band (its oracle logit within `tie` of the maximum)."""
+    tok_gpu = np.asarray(tok_gpu)
+    bad = []
+    for i in range(len(tok_or)):
+        if tok_gpu[i] == tok_or[i]:
+            continue
+        if gap_or[i] < tie and z_or[i, tok_gpu[i]] >= z_or[i].max() - tie:
+            continue
+        bad.append((i, int(tok_gpu[i]), int(tok_or[i]), float(gap_or[i])))
+    return bad

@@ -1,0 +1,90 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lossless_kv_cache_vc_amd import vc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "vc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(vc.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    lib = vc.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert vc.version().startswith("vc ")
+
+
+def _shape(**kw):
+    s = dict(L=2, Hq=8, Hkv=2, d=128, max_rows=32)
+    s.update(kw)
+    return vc.shape(s["L"], s["Hq"], s["Hkv"], s["d"], s["max_rows"])
+
+
+class _FakeTensor:
+    """Something with a data_ptr(): host validation never dereferences device pointers."""
+    def __init__(self, addr, shape=(1, 4)):
+        self.addr, self.shape = addr, shape
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _pool(bits=16):
+    t = _FakeTensor(0x1000, (4, 8))
+    return vc.PagedPool(bits, t, t, t, 16, t if bits != 16 else None, t if bits != 16 else None)
+
+
+def _expect(code, fn):
+    with pytest.raises(vc.VCError) as e:
+        fn()
+    assert e.value.code == code, str(e.value)
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device pointers; host-only check")
+def test_host_validation_rejects_bad_arguments():
+    t = _FakeTensor(0x1000)
+    ok_req = vc.Req(0, 0, 100, 0, 0, 8, vc.VC_VERIFY)
+    call = lambda shp, reqs, pool=_pool(), ws=None: vc.verify_attn(shp, reqs, t, t, t, pool, t, ws, 0, 0)
+    _expect(vc.VC_EUNSUPPORTED, lambda: call(_shape(d=96), [ok_req]))
+    _expect(vc.VC_EINVAL, lambda: call(_shape(Hq=6, Hkv=4), [ok_req]))
+    _expect(vc.VC_EINVAL, lambda: call(_shape(max_rows=24), [ok_req]))
+    _expect(vc.VC_EINVAL, lambda: call(_shape(), [vc.Req(0, 0, 100, 0, 30, 8, vc.VC_VERIFY)]))  # q0+rows > max
+    _expect(vc.VC_EINVAL, lambda: call(_shape(), [vc.Req(0, 0, -1, 0, 0, 8, vc.VC_VERIFY)]))
+    _expect(vc.VC_EINVAL, lambda: call(_shape(), [vc.Req(0, 0, 16 * 9, 0, 0, 8, vc.VC_VERIFY)]))  # > max_pages
+    _expect(vc.VC_EINVAL, lambda: call(_shape(), [ok_req], pool=_pool(bits=3)))
+    _expect(vc.VC_EINVAL, lambda: call(_shape(), [ok_req], pool=_pool(bits=2)))  # verify needs bf16
+    _expect(vc.VC_EINVAL, lambda: vc.draft_attn(_shape(Hq=32, Hkv=2), [vc.Req(0, 0, 10, 0, 0, 2, 1)],
+                                                 t, t, t, _pool(), t, None, 0, 0))  # rows*G > 16
+    _expect(vc.VC_EINVAL, lambda: vc.verify_attn(_shape(), [ok_req], t, t, t, _pool(), t, None, 6, 0))
+    # splitting needs a workspace
+    _expect(vc.VC_ENOSPACE, lambda: vc.verify_attn(_shape(), [vc.Req(0, 0, 120, 0, 0, 8, 0)], t, t, t,
+                                                   _pool(), t, None, 4, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.accept(1, 65, 65, 10, t, t, t, t, t, t, t, t, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.logits(4, 8, 8, t, 4, t, t, 0))
+
+
+def test_workspace_size_accounts_for_splits():
+    shp = _shape()
+    r = vc.Req(0, 0, 16 * 100, 0, 0, 8, vc.VC_VERIFY)
+    assert vc.attn_workspace_size(shp, [r], 400) == 0            # one split
+    # 100 pages in chunks of 40 -> 3 splits of 8 rows * 4 heads, d + 4 floats each
+    assert vc.attn_workspace_size(shp, [r], 40) == 2 * 2 * 3 * 8 * 4 * 132 * 4
