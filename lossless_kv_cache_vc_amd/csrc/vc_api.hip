@@ -153,8 +153,8 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
     d.q0 = r.q0;
     d.rows = r.rows;
     d.kind = r.kind;
-    d.chunk_pages = chunk;
-    d.nsplit = pages > 0 ? (pages + chunk - 1) / chunk : 1;
+    const int target = std::min(chunk, kMaxChunkPages);
+    d.chunk_pages = split_context(pages, target, &d.nsplit);
     d.nrg = r.kind == VC_VERIFY ? (r.rows * G + 127) / 128 : 1;
     d.item_base = (int32_t)items;
     items += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * d.nrg;
@@ -226,7 +226,9 @@ size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req*
   size_t floats = 0;
   for (int i = 0; i < num_reqs; ++i) {
     const int pages = (reqs[i].ctx_len + kBlock - 1) / kBlock;
-    const int nsplit = pages > 0 ? (pages + chunk - 1) / chunk : 1;
+    const int target = std::min(chunk, kMaxChunkPages);
+    int nsplit;
+    split_context(pages, target, &nsplit);
     if (nsplit > 1)
       floats += (size_t)shape->num_layers * shape->num_kv_heads * nsplit * reqs[i].rows * G *
                 (shape->head_dim + 4);

@@ -26,10 +26,8 @@ namespace vc {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTileKeys = 64;        // keys per verify tile (4 pages)
-constexpr int kRowsPerGroup = 32 * kWaves;
+constexpr int kDWaves = 4;            // waves of a draft-only work-group
+constexpr int kDThreads = 64 * kDWaves;
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -105,9 +103,11 @@ struct PageRef {
   int bpos;   // drafted block: block position of token 0
 };
 
+// Descriptors are held by value: a pointer into the kernel's argument block would make the
+// compiler copy the whole block to scratch memory.
 struct ItemCtx {
-  const ReqDev* rq;
-  const PoolDev* pool;
+  ReqDev rq;
+  PoolDev pool;
   int l, g, split;
   int nctx, nbk, npages, p_lo;
   int rows_total;
@@ -119,9 +119,9 @@ __device__ __forceinline__ PageRef page_ref(const AttnArgs& a, const ItemCtx& it
   PageRef pr;
   pr.k = pr.v = pr.ksz = pr.vsz = nullptr;
   pr.bpos = 0;
-  const ReqDev& rq = *it.rq;
+  const ReqDev& rq = it.rq;
   if (ip < it.nctx) {
-    const PoolDev& pl = *it.pool;
+    const PoolDev& pl = it.pool;
     int p = it.p_lo + ip;
     int phys = pl.page_table[(int64_t)rq.page_row * pl.max_pages + p];
     if (phys < 0 || phys >= pl.nblk) {  // an invalid table entry reads as an empty page
@@ -171,7 +171,7 @@ __device__ __forceinline__ bool key_visible(const PageRef& pr, int tt, int qpos)
 template <int D>
 __device__ __forceinline__ float* out_row(const AttnArgs& a, const ItemCtx& it, int row,
                                           bool* partial) {
-  const ReqDev& rq = *it.rq;
+  const ReqDev& rq = it.rq;
   if (rq.nsplit == 1) {
     *partial = false;
     int tok = row / a.G, jh = row % a.G;
@@ -183,37 +183,149 @@ __device__ __forceinline__ float* out_row(const AttnArgs& a, const ItemCtx& it, 
   return a.part + rq.part_base + prow * (D + 4);
 }
 
-// ------------------------------------------------------------------ verify path (32x32x16)
-template <int D>
-struct VerifySmem {
-  static constexpr int kStageK = kTileKeys * D * 2;  // bytes
-  static constexpr int kStage = 2 * kStageK;          // K then V
-  static constexpr int kBytes = 2 * kStage;           // double buffered
-};
-
 // key slot of MFMA row M within a 32-key block: lanes' accumulator registers then hold
 // 8 consecutive tokens of one page, which is the B-operand order of the value product.
 __device__ __forceinline__ int key_of_m32(int M) {
   return 16 * (M >> 4) + 8 * ((M >> 2) & 1) + 4 * ((M >> 3) & 1) + (M & 3);
 }
 
+// XOR swizzle of the 16-byte chunks of a key row in LDS (bank-conflict-free MFMA operand reads)
 template <int D>
 __device__ __forceinline__ int swz_k(int key) {
   return D == 128 ? (key & 15) : ((key >> 1) & 7);
 }
 
+// ------------------------------------------------------------------ verify path (32x32x16)
+// A verify work-group has 8 waves: wave w owns row block w & 3 (32 query rows) and key half
+// w >> 2 of every 64-key tile.  K/V pages move from HBM straight into a 4-stage LDS ring with
+// gfx950's global_load_lds_dwordx4 (no register staging), three tiles ahead of the one being
+// consumed; each wave moves one 4 KB page of every tile (waves 0-3 keys, 4-7 values), so each
+// wave's vmcnt counts its own share of the ring.  The two key halves of a row block are merged
+// through LDS at the end.
+constexpr int kVWaves = 8;
+constexpr int kVThreads = 64 * kVWaves;
+constexpr int kVStages = 4;
+
+template <int D>
+struct VRing {
+  static constexpr int kPage = kBlock * D * 2;      // bytes of one K or V page
+  static constexpr int kTileK = 4 * kPage;          // 64 keys
+  static constexpr int kStage = 2 * kTileK;         // keys then values
+  static constexpr int kRing = kVStages * kStage;
+  static constexpr int kIds = kRing;                // LDS offset of the page ids
+  static constexpr int kBytes = kRing + kMaxChunkPages * 4;
+  static constexpr int kLoads = kPage / 1024;       // 16-byte-per-lane loads per wave per tile
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// wait until at most N (< 64) of this wave's vector memory loads are outstanding (loads
+// complete in issue order).  gfx9 s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] and
+// lgkmcnt [11:8] (the last two left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Work-group barrier of the ring loop.  It carries no release fence: a release would wait for
+// the ring's in-flight LDS loads as if they were pending LDS stores.  None is needed: LDS is
+// written only by those loads, whose completion each wave establishes with wait_vmem() before
+// the barrier, and every LDS read of the previous tile has been consumed (by the MFMAs) before
+// the barrier.  The acquire fence keeps the next tile's LDS reads and the following ring loads
+// below the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct VPage {
+  int kind;   // 0 context, 1 drafted block, 2 none
+  int valid;  // tokens present
+  int bpos;   // drafted block position of token 0
+};
+
+__device__ __forceinline__ VPage vpage_info(const ItemCtx& it, const int32_t* ids, int ip) {
+  VPage p;
+  p.bpos = 0;
+  const ReqDev& rq = it.rq;
+  if (ip < it.nctx) {
+    p.kind = ids[ip] < 0 ? 2 : 0;
+    p.valid = p.kind == 0 ? min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip)) : 0;
+  } else if (ip < it.npages) {
+    const int j = ip - it.nctx;
+    p.kind = 1;
+    p.valid = min(kBlock, rq.q0 + rq.rows - kBlock * j);
+    p.bpos = kBlock * j;
+  } else {
+    p.kind = 2;
+    p.valid = 0;
+  }
+  return p;
+}
+
+__device__ __forceinline__ bool vkey_visible(const VPage& p, int tt, int qpos) {
+  return tt < p.valid && (p.kind == 0 || p.bpos + tt <= qpos);
+}
+
+// Issue this wave's share of tile `t` into ring stage t % 4: one K page (waves 0-3) or one V
+// page (waves 4-7).  A missing page reads block 0 of the pool (always in bounds) and is masked
+// when consumed, so every wave issues the same number of loads per tile.  The K and V cases are
+// separate code paths: choosing between the descriptor fields by reference would make the
+// compiler copy the whole kernel argument block to scratch.
+template <int D, bool V>
+__device__ __forceinline__ void verify_issue_kv(const uint8_t* pool_base, const uint16_t* blk,
+                                                const AttnArgs& a, const ItemCtx& it,
+                                                const int32_t* ids, uint8_t* smem, int t, int ps,
+                                                int lane) {
+  using R = VRing<D>;
+  const int ip = 4 * t + ps;
+  const uint8_t* page;
+  if (ip < it.nctx || ip >= it.npages) {
+    int phys = ip < it.nctx ? ids[ip] : 0;
+    if (phys < 0) phys = 0;
+    page = pool_base + (((int64_t)it.l * it.pool.nblk + phys) * a.Hkv + it.g) * R::kPage;
+  } else {
+    const int64_t unit = (((int64_t)it.rq.slot * a.L + it.l) * a.Hkv + it.g) * (a.xmax / kBlock) +
+                         (ip - it.nctx);
+    page = reinterpret_cast<const uint8_t*>(blk) + unit * R::kPage;
+  }
+  uint8_t* dst = smem + (t & (kVStages - 1)) * R::kStage + (V ? R::kTileK : 0) + ps * R::kPage;
+#pragma unroll
+  for (int i = 0; i < R::kLoads; ++i) {
+    int off;
+    if constexpr (!V) {
+      constexpr int CPR = D / 8;           // 16-byte chunks per key row
+      constexpr int RPI = 1024 / (2 * D);  // key rows per load
+      const int tok = RPI * i + lane / CPR, slot = lane % CPR;
+      off = tok * (2 * D) + ((slot ^ swz_k<D>(tok)) * 16);
+    } else {
+      const int dd = 32 * i + (lane >> 1), slot = lane & 1;
+      off = dd * 32 + ((slot ^ ((dd >> 3) & 1)) * 16);
+    }
+    __builtin_amdgcn_global_load_lds(page + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void verify_issue(const AttnArgs& a, const ItemCtx& it, const int32_t* ids,
+                                             uint8_t* smem, int t, int w, int lane) {
+  if (w < 4) verify_issue_kv<D, false>(it.pool.k, a.blk_k, a, it, ids, smem, t, w & 3, lane);
+  else verify_issue_kv<D, true>(it.pool.v, a.blk_v, a, it, ids, smem, t, w & 3, lane);
+}
+
 template <int D>
 __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
-  constexpr int CPP = 2 * D;                 // 16-byte chunks per page (K or V)
-  constexpr int NCH = 4 * CPP / kThreads;    // chunks per thread per tensor per tile
-  constexpr int CPR = D / 8;                 // chunks per key row
-  constexpr int NS = D / 16;                 // MFMA k-steps of the score product
-  constexpr int ND = D / 32;                 // 32-wide d blocks of the output
+  using R = VRing<D>;
+  constexpr int NS = D / 16;  // MFMA k-steps of the score product
+  constexpr int ND = D / 32;  // 32-wide d blocks of the output
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const ReqDev& rq = *it.rq;
+  const int rb = w & 3, kh = w >> 2;
+  const ReqDev& rq = it.rq;
   const int G = a.G;
-  const int row = rg * kRowsPerGroup + 32 * w + n;
-  const bool wave_on = rg * kRowsPerGroup + 32 * w < it.rows_total;
+  const int row = rg * 128 + 32 * rb + n;
+  const bool wave_on = rg * 128 + 32 * rb < it.rows_total;
   const bool row_ok = row < it.rows_total;
   const int tok = row_ok ? row / G : 0;
   const int qpos = rq.q0 + tok;
@@ -227,167 +339,382 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
     for (int s = 0; s < NS; ++s) qreg[s] = row_ok ? ld16(qp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
   }
 
+  // block ids of this item's context pages (invalid entries become -1)
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + R::kIds);
+  {
+    const PoolDev& pl = it.pool;
+    const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
+    for (int i = tid; i < it.nctx; i += kVThreads) {
+      const int phys = pt[i];
+      ids[i] = (phys < 0 || phys >= pl.nblk) ? -1 : phys;
+    }
+  }
+  // the query registers and page ids are complete before the first ring load is issued, so the
+  // loop's vmcnt waits cover ring loads only
+  wait_vmem<0>();
+  __syncthreads();
+
+  const int ntiles = (it.npages + 3) >> 2;
+#pragma unroll
+  for (int t = 0; t < kVStages - 1; ++t)
+    if (t < ntiles) verify_issue<D>(a, it, ids, smem, t, w, lane);
+
   f32x16 acc_o[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc_o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
-
-  const int ntiles = (it.npages + 3) >> 2;
-  u32x4 kbuf[NCH], vbuf[NCH];
-
-  // chunk j of this thread: page (j * kThreads + tid) / CPP, which is j for d = 128 and
-  // 2j + (tid >= 128) for d = 64 (uniform per wave either way)
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + kThreads * j;
-      const int off = c % CPP;
-      PageRef p;
-      if (CPP == kThreads) {
-        p = page_ref<D>(a, it, 4 * t + j, false);
-      } else {
-        const PageRef p0 = page_ref<D>(a, it, 4 * t + 2 * j, false);
-        const PageRef p1 = page_ref<D>(a, it, 4 * t + 2 * j + 1, false);
-        p = (tid >= CPP) ? p1 : p0;
-      }
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (p.kind != 2) {
-        const int ktok = off / CPR;
-        if (ktok < p.valid) kv = ld16(p.k + off * 16);
-        vv = ld16(p.v + off * 16);
-        if (p.valid < kBlock) vv = mask_tokens(vv, (off & 1) * 8, p.valid);
-      }
-      kbuf[j] = kv;
-      vbuf[j] = vv;
-    }
-  };
-  auto store_tile = [&](int st) {
-    uint8_t* sk = smem + st * VerifySmem<D>::kStage;
-    uint8_t* sv = sk + VerifySmem<D>::kStageK;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + kThreads * j;
-      const int ps = (CPP == kThreads) ? j : 2 * j + (tid >= CPP ? 1 : 0), off = c % CPP;
-      const int key = ps * kBlock + off / CPR, cc = off % CPR;
-      *reinterpret_cast<u32x4*>(sk + key * (2 * D) + ((cc ^ swz_k<D>(key)) * 16)) = kbuf[j];
-      const int dd = off >> 1, half = off & 1;
-      *reinterpret_cast<u32x4*>(sv + (ps * D + dd) * 32 + ((half ^ ((dd >> 3) & 1)) * 16)) = vbuf[j];
-    }
-  };
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  const int key = 32 * kh + key_of_m32(n);
+  const int ksw = swz_k<D>(key);
 
   for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    const int ahead = min(kVStages - 2, ntiles - 1 - t);  // tiles issued after t
+    if (ahead >= 2) wait_vmem<2 * R::kLoads>();
+    else if (ahead == 1) wait_vmem<R::kLoads>();
+    else wait_vmem<0>();
+    ring_barrier();  // tile t is in LDS for every wave; stage (t - 1) is free
+    if (t + kVStages - 1 < ntiles) verify_issue<D>(a, it, ids, smem, t + kVStages - 1, w, lane);
+    if (!wave_on) continue;
 
-    if (wave_on) {
-      const uint8_t* sk = smem + st * VerifySmem<D>::kStage;
-      const uint8_t* sv = sk + VerifySmem<D>::kStageK;
-      f32x16 s_acc[2];
+    const uint8_t* sk = smem + (t & (kVStages - 1)) * R::kStage;
+    const uint8_t* sv = sk + R::kTileK;
+    f32x16 s_acc = f32x16{};
+    const uint8_t* krow = sk + key * (2 * D);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s_acc[kb] = f32x16{};
-        const int key = 32 * kb + key_of_m32(n);
-        const uint8_t* krow = sk + key * (2 * D);
-        const int sw = swz_k<D>(key);
+    for (int s = 0; s < NS; ++s) {
+      const u32x4 av = ld16(krow + (((2 * s + h) ^ ksw) * 16));
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(qreg[s]), s_acc, 0, 0, 0);
+    }
+    // register r holds key (page 2*kh + r/8, token 8h + r%8) of row n
+    const VPage p0 = vpage_info(it, ids, 4 * t + 2 * kh);
+    const VPage p1 = vpage_info(it, ids, 4 * t + 2 * kh + 1);
+    const bool full = p0.kind == 0 && p0.valid == kBlock && p1.kind == 0 && p1.valid == kBlock;
+    if (!full) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          u32x4 av = ld16(krow + (((2 * s + h) ^ sw) * 16));
-          s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(qreg[s]), s_acc[kb],
-                                                              0, 0, 0);
-        }
-      }
-      // masking: only tiles holding a partial or drafted-block page need it
-      PageRef pr[4];
-      bool need_mask = false;
+      for (int r = 0; r < 16; ++r)
+        if (!vkey_visible(r < 8 ? p0 : p1, 8 * h + (r & 7), qpos)) s_acc[r] = -INFINITY;
+    }
+    float mloc = -INFINITY;
 #pragma unroll
-      for (int ps = 0; ps < 4; ++ps) {
-        pr[ps] = page_ref<D>(a, it, 4 * t + ps, false);
-        need_mask |= (pr[ps].kind != 0) || (pr[ps].valid < kBlock);
-      }
-      if (need_mask) {
+    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s_acc[r]);
+    mloc = wave_xor_max(mloc, 32);
+    const float m_new = fmaxf(m_run, mloc * sc);
+    if (__any(m_new > m_run + kLazyRescale)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < ND; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ps = 2 * kb + (r >> 3), tt = 8 * h + (r & 7);
-            if (!key_visible(pr[ps], tt, qpos)) s_acc[kb][r] = -INFINITY;
-          }
-      }
-      float mloc = -INFINITY;
+        for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    uint32_t pb[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < 16; r += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s_acc[r], sc, -m_use));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s_acc[r + 1], sc, -m_use));
+      l_run += e0 + e1;
+      pb[r >> 1] = pack_bf16(e0, e1);
+    }
+    // O^T += V^T P^T, one page (16 keys) per k-step
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s_acc[kb][r]);
-      mloc = wave_xor_max(mloc, 32);
-      const float m_new = fmaxf(m_run, mloc * sc);
-      if (__any(m_new > m_run + kLazyRescale)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
+    for (int pj = 0; pj < 2; ++pj) {
+      const u32x4 bv = {pb[4 * pj], pb[4 * pj + 1], pb[4 * pj + 2], pb[4 * pj + 3]};
+      const VPage& pp = pj ? p1 : p0;
+      const uint8_t* vpg = sv + (2 * kh + pj) * (D * 32);
 #pragma unroll
-        for (int i = 0; i < ND; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
-      uint32_t pb[2][8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][r], sc, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][r + 1], sc, -m_use));
-          lsum += p0 + p1;
-          pb[kb][r >> 1] = pack_bf16(p0, p1);
-        }
-      l_run += lsum;
-      // O^T += V^T P^T, one page (16 keys) per k-step
-#pragma unroll
-      for (int pj = 0; pj < 4; ++pj) {
-        const int kb = pj >> 1, hf = pj & 1;
-        u32x4 bv = {pb[kb][4 * hf], pb[kb][4 * hf + 1], pb[kb][4 * hf + 2], pb[kb][4 * hf + 3]};
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const int dd = 32 * db + n;
-          u32x4 av = ld16(sv + (pj * D + dd) * 32 + ((h ^ ((dd >> 3) & 1)) * 16));
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(bv), acc_o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < ND; ++db) {
+        const int dd = 32 * db + n;
+        u32x4 av = ld16(vpg + dd * 32 + ((h ^ ((dd >> 3) & 1)) * 16));
+        if (!full && !(pp.kind == 0 && pp.valid == kBlock)) av = mask_tokens(av, 8 * h, pp.valid);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(bv), acc_o[db], 0, 0, 0);
       }
     }
-
-    if (t + 1 < ntiles) store_tile(st ^ 1);
-    __syncthreads();
   }
 
-  if (!wave_on) return;
-  const float l_tot = wave_xor_sum(l_run, 32);
+  // merge the two key halves of every row block through LDS (the ring is free now)
+  __syncthreads();
+  constexpr int NR = ND * 16;  // accumulator floats per lane
+  float* red = reinterpret_cast<float*>(smem) + rb * (64 * (NR + 2));
+  if (kh == 1 && wave_on) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(red + ((db * 4 + q) * 64 + lane) * 4) =
+            f32x4{acc_o[db][4 * q], acc_o[db][4 * q + 1], acc_o[db][4 * q + 2], acc_o[db][4 * q + 3]};
+    red[NR * 64 + lane] = m_run;
+    red[NR * 64 + 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1 || !wave_on) return;
+  const float m1 = red[NR * 64 + lane], l1 = red[NR * 64 + 64 + lane];
+  const float M = fmaxf(m_run, m1);
+  const float f0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+  const float l_tot = wave_xor_sum(f0 * l_run + f1 * l1, 32);
   if (!row_ok) return;
   bool partial;
   float* dst = out_row<D>(a, it, row, &partial);
-  const float inv = partial ? 1.f : 1.f / l_tot;
+  const float inv = partial ? 1.f : (l_tot > 0.f ? 1.f / l_tot : 0.f);
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f32x4 o = {acc_o[db][4 * q] * inv, acc_o[db][4 * q + 1] * inv, acc_o[db][4 * q + 2] * inv,
-                 acc_o[db][4 * q + 3] * inv};
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(red + ((db * 4 + q) * 64 + lane) * 4);
+      f32x4 o = {acc_o[db][4 * q], acc_o[db][4 * q + 1], acc_o[db][4 * q + 2], acc_o[db][4 * q + 3]};
+      o = (f0 * o + f1 * o1) * inv;
       *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q + 4 * h) = o;
     }
   if (partial && h == 0) {
-    dst[D] = m_run;
+    dst[D] = M;
     dst[D + 1] = l_tot;
   }
 }
 
-// ------------------------------------------------------------------ draft path (16x16x32)
+// Combine the NW waves' softmax states of a draft item (rows n < 16, lane (n, kg) holding
+// channels 16 db + 4 kg .. + 3) through LDS and write the rows (or the split partials).
+template <int D, int NW>
+__device__ __forceinline__ void draft_merge(const AttnArgs& a, const ItemCtx& it, uint8_t* smem,
+                                            const f32x4* acc_o, float m_run, float l_run) {
+  constexpr int ND = D / 16;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  float* red = reinterpret_cast<float*>(smem);  // [wave][16 rows][D + 4]
+  constexpr int RS = D + 4;
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+    *reinterpret_cast<f32x4*>(red + (w * 16 + n) * RS + 16 * db + 4 * kg) = acc_o[db];
+  if (kg == 0) {
+    red[(w * 16 + n) * RS + D] = m_run;
+    red[(w * 16 + n) * RS + D + 1] = l_run;
+  }
+  __syncthreads();
+  constexpr int NQ = D / 4;  // float4 chunks per row
+  for (int task = tid; task < 16 * NQ; task += 64 * NW) {
+    const int rr = task / NQ, cq = task % NQ;
+    if (rr >= it.rows_total) continue;
+    float mw[NW], M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      mw[ww] = red[(ww * 16 + rr) * RS + D];
+      M = fmaxf(M, mw[ww]);
+    }
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = (mw[ww] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[ww] - M);
+      lsum += f * red[(ww * 16 + rr) * RS + D + 1];
+      const f32x4 ow = *reinterpret_cast<const f32x4*>(red + (ww * 16 + rr) * RS + 4 * cq);
+      o += f * ow;
+    }
+    bool partial;
+    float* dst = out_row<D>(a, it, rr, &partial);
+    if (!partial) o *= lsum > 0.f ? 1.f / lsum : 0.f;
+    *reinterpret_cast<f32x4*>(dst + 4 * cq) = o;
+    if (partial && cq == 0) {
+      dst[D] = M;
+      dst[D + 1] = lsum;
+    }
+  }
+}
+
+
+// ------------------------------------------------------------------ draft path, bf16 caches
+// A draft step has G <= 16 query rows, so the work is a stream over the item's pages with little
+// arithmetic per byte.  Every wave takes pages w, w + NW, w + 2 NW, ... of the item and streams
+// them through a private ring of STG one-page slots (keys then values) in LDS, filled with
+// global_load_lds_dwordx4 STG - 1 pages ahead; a wave reads only what it loaded itself, so the
+// loop has no barrier, only the wave's own vmcnt wait.  Scores S^T = K Q^T use
+// v_mfma_f32_16x16x32_bf16 (rows padded to 16); the softmax weights then sit exactly where the
+// B operand of v_mfma_f32_16x16x16_bf16 wants them for O^T += V^T P^T.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct DRing {
+  static constexpr int kPage = kBlock * D * 2;  // bytes of one K or V page
+  static constexpr int kSlot = 2 * kPage;       // one page of keys then one of values
+  static constexpr int kLoads = kPage / 1024;   // 16-byte-per-lane loads per page and tensor
+  static constexpr int kRing = 16 * kSlot;      // LDS of all waves' rings (4 x 4 or 8 x 2 slots)
+  static constexpr int kIds = kRing;
+  static constexpr int kBytes = kRing + kMaxChunkPages * 4;
+};
+
+// XOR swizzle of a key row's 16-byte chunks (conflict-free 16-byte reads of 16 rows)
+template <int D>
+__device__ __forceinline__ int dswz(int tok) {
+  return D == 128 ? (tok & 15) : (tok & 7);
+}
+
+// wait for this wave's loads of the page it consumes next (N loads may stay in flight), then
+// keep the compiler from moving LDS reads above the wait
+template <int N>
+__device__ __forceinline__ void ring_wait_own() {
+  wait_vmem<N>();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, bool V>
+__device__ __forceinline__ void draft_issue_kv(const uint8_t* pool_base, const uint16_t* blk,
+                                               const AttnArgs& a, const ItemCtx& it,
+                                               const int32_t* ids, uint8_t* slot, int ip, int lane) {
+  using R = DRing<D>;
+  const uint8_t* page;
+  if (ip < it.nctx || ip >= it.npages) {
+    int phys = ip < it.nctx ? ids[ip] : 0;
+    if (phys < 0) phys = 0;  // missing page: block 0 (in bounds), masked when consumed
+    page = pool_base + (((int64_t)it.l * it.pool.nblk + phys) * a.Hkv + it.g) * R::kPage;
+  } else {
+    const int64_t unit = (((int64_t)it.rq.slot * a.L + it.l) * a.Hkv + it.g) * (a.xmax / kBlock) +
+                         (ip - it.nctx);
+    page = reinterpret_cast<const uint8_t*>(blk) + unit * R::kPage;
+  }
+  uint8_t* dst = slot + (V ? R::kPage : 0);
+#pragma unroll
+  for (int i = 0; i < R::kLoads; ++i) {
+    int off;
+    if constexpr (!V) {
+      constexpr int CPR = D / 8;
+      constexpr int RPI = 1024 / (2 * D);
+      const int tok = RPI * i + lane / CPR, s = lane % CPR;
+      off = tok * (2 * D) + ((s ^ dswz<D>(tok)) * 16);
+    } else {
+      const int dd = 32 * i + (lane >> 1), s = lane & 1;
+      off = dd * 32 + ((s ^ ((dd >> 2) & 1)) * 16);
+    }
+    __builtin_amdgcn_global_load_lds(page + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
+  }
+}
+
+// zero the bf16 lanes t (0..3) of an 8-byte chunk with first + t >= valid
+__device__ __forceinline__ u32x2 mask_tokens4(u32x2 v, int first, int valid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t x = v[i];
+    if (first + 2 * i >= valid) x &= 0xFFFF0000u;
+    if (first + 2 * i + 1 >= valid) x &= 0x0000FFFFu;
+    v[i] = x;
+  }
+  return v;
+}
+
+template <int D, int NW, int STG>
+__device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
+  using R = DRing<D>;
+  static_assert(NW * STG * R::kSlot <= R::kRing, "draft rings exceed their LDS");
+  constexpr int NS = D / 32;  // k-steps of the score product
+  constexpr int ND = D / 16;  // 16-wide d blocks of the output
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const ReqDev& rq = it.rq;
+  const int G = a.G;
+  const bool row_ok = n < it.rows_total;
+  const int tok = row_ok ? n / G : 0;
+  const int qpos = rq.q0 + tok;
+
+  u32x4 qreg[NS];
+  {
+    const uint16_t* qp = a.q + ((((int64_t)rq.slot * a.L + it.l) * a.xmax + rq.q0 + tok) * a.Hq +
+                                it.g * G + (row_ok ? n % G : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qreg[s] = row_ok ? ld16(qp + 32 * s + 8 * kg) : u32x4{0, 0, 0, 0};
+  }
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + R::kIds);
+  {
+    const PoolDev& pl = it.pool;
+    const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
+    for (int i = tid; i < it.nctx; i += 64 * NW) {
+      const int phys = pt[i];
+      ids[i] = (phys < 0 || phys >= pl.nblk) ? -1 : phys;
+    }
+  }
+  wait_vmem<0>();
+  __syncthreads();
+
+  uint8_t* ring = smem + w * (STG * R::kSlot);
+  const int mine = it.npages > w ? (it.npages - w + NW - 1) / NW : 0;
+  auto issue = [&](int k) {
+    uint8_t* slot = ring + (k % STG) * R::kSlot;
+    const int ip = w + NW * k;
+    draft_issue_kv<D, false>(it.pool.k, a.blk_k, a, it, ids, slot, ip, lane);
+    draft_issue_kv<D, true>(it.pool.v, a.blk_v, a, it, ids, slot, ip, lane);
+  };
+#pragma unroll
+  for (int k = 0; k < STG - 1; ++k)
+    if (k < mine) issue(k);
+
+  f32x4 acc_o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc_o[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+  constexpr int PER = 2 * R::kLoads;  // loads per page
+
+  for (int k = 0; k < mine; ++k) {
+    const int ahead = min(STG - 2, mine - 1 - k);
+    if (STG > 3 && ahead >= 2) ring_wait_own<2 * PER>();
+    else if (STG > 2 && ahead >= 1) ring_wait_own<PER>();
+    else ring_wait_own<0>();
+    if (k + STG - 1 < mine) issue(k + STG - 1);
+
+    const uint8_t* sk = ring + (k % STG) * R::kSlot;
+    const uint8_t* sv = sk + R::kPage;
+    // S^T: lane (n, kg) ends with keys 4kg..4kg+3 of row n
+    f32x4 s_acc = f32x4{};
+    {
+      const uint8_t* krow = sk + n * (2 * D);
+      const int sw = dswz<D>(n);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 av = ld16(krow + (((4 * s + kg) ^ sw) * 16));
+        s_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(qreg[s]), s_acc, 0, 0, 0);
+      }
+    }
+    const VPage pg = vpage_info(it, ids, w + NW * k);
+    const bool full = pg.kind == 0 && pg.valid == kBlock;
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!vkey_visible(pg, 4 * kg + i, qpos)) s_acc[i] = -INFINITY;
+    }
+    float mloc = fmaxf(fmaxf(s_acc[0], s_acc[1]), fmaxf(s_acc[2], s_acc[3]));
+    mloc = wave_xor_max(mloc, 16);
+    mloc = wave_xor_max(mloc, 32);
+    const float m_new = fmaxf(m_run, mloc * sc);
+    if (__any(m_new > m_run + kLazyRescale)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) acc_o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s_acc[i], sc, -m_use));
+    l_run += (e[0] + e[1]) + (e[2] + e[3]);
+    const u32x2 pbits = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3])};
+    const s16x4 pv = __builtin_bit_cast(s16x4, pbits);
+    // O^T += V^T P^T: lane (m, kg) feeds channel 16 db + m, tokens 4kg..4kg+3
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int dd = 16 * db + n;
+      u32x2 av = *reinterpret_cast<const u32x2*>(sv + dd * 32 + ((((kg >> 1) ^ ((dd >> 2) & 1))) * 16) +
+                                                 (kg & 1) * 8);
+      if (!full) av = mask_tokens4(av, 4 * kg, pg.valid);
+      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av), pv, acc_o[db],
+                                                            0, 0, 0);
+    }
+  }
+
+  // ---- merge the waves' states through LDS (rings are free once every wave is here)
+  __syncthreads();
+  l_run = wave_xor_sum(l_run, 16);
+  l_run = wave_xor_sum(l_run, 32);
+  draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
+}
+
+// ------------------------------------------------------------------ draft path, KIVI caches (16x16x32)
 // Channel order of the draft path: lane group kg (lane / 16) owns channels [kg*D/4, (kg+1)*D/4)
 // and k-step s covers 8 of them, so a lane's codes of one key row are contiguous.
 template <int D>
@@ -409,13 +736,13 @@ __device__ __forceinline__ void unpack8(const uint32_t* words, int u0, float* ou
   }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int NW>
 __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   constexpr bool KIVI = BITS != 16;
   constexpr int NS = D / 32;   // k-steps of the score product (16x16x32)
   constexpr int ND = D / 16;   // 16-wide d blocks of the output
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
-  const ReqDev& rq = *it.rq;
+  const ReqDev& rq = it.rq;
   const int G = a.G;
   const bool row_ok = n < it.rows_total;
   const int tok = row_ok ? n / G : 0;
@@ -441,7 +768,7 @@ __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) 
   const float sc = a.scale_log2;
   const int npairs = (it.npages + 1) >> 1;
 
-  for (int pp = w; pp < npairs; pp += kWaves) {
+  for (int pp = w; pp < npairs; pp += NW) {
     PageRef pr[2];
     pr[0] = page_ref<D>(a, it, 2 * pp, KIVI);
     pr[1] = page_ref<D>(a, it, 2 * pp + 1, KIVI);
@@ -567,91 +894,95 @@ __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) 
     }
   }
 
-  // ---- merge the 4 waves' states through LDS
+  // ---- merge the waves' states through LDS
   l_run = wave_xor_sum(l_run, 16);
   l_run = wave_xor_sum(l_run, 32);
-  float* red = reinterpret_cast<float*>(smem);  // [wave][16 rows][D + 4]
-  constexpr int RS = D + 4;
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-    *reinterpret_cast<f32x4*>(red + (w * 16 + n) * RS + 16 * db + 4 * kg) = acc_o[db];
-  if (kg == 0) {
-    red[(w * 16 + n) * RS + D] = m_run;
-    red[(w * 16 + n) * RS + D + 1] = l_run;
-  }
-  __syncthreads();
-  constexpr int NQ = D / 4;  // float4 chunks per row
-  for (int task = tid; task < 16 * NQ; task += kThreads) {
-    const int rr = task / NQ, cq = task % NQ;
-    if (rr >= it.rows_total) continue;
-    float mw[kWaves], M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      mw[ww] = red[(ww * 16 + rr) * RS + D];
-      M = fmaxf(M, mw[ww]);
-    }
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = (mw[ww] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[ww] - M);
-      lsum += f * red[(ww * 16 + rr) * RS + D + 1];
-      const f32x4 ow = *reinterpret_cast<const f32x4*>(red + (ww * 16 + rr) * RS + 4 * cq);
-      o += f * ow;
-    }
-    bool partial;
-    float* dst = out_row<D>(a, it, rr, &partial);
-    if (!partial) o *= 1.f / lsum;
-    *reinterpret_cast<f32x4*>(dst + 4 * cq) = o;
-    if (partial && cq == 0) {
-      dst[D] = M;
-      dst[D + 1] = lsum;
-    }
-  }
+  draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
 }
 
-// MODE 0: verify items only, 1: draft items only, 2: both (one launch over a mixed batch)
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[VerifySmem<D>::kBytes];
-  // consecutive items run on the same XCD (work-groups are dealt round-robin over 8 XCDs)
+template <int D>
+struct DraftSmem {
+  static constexpr int kBytes = kDWaves * 16 * (D + 4) * 4;  // per-wave softmax states
+};
+
+// Work item -> (request, row group, split, kv head, layer).  Work-groups are dealt round-robin
+// over the 8 XCDs; consecutive items are mapped to one XCD so that items that share K/V (row
+// groups of one unit) run on the same L2.
+__device__ __forceinline__ bool decode_item(const AttnArgs& a, ItemCtx* it, int* rg) {
   const int b = blockIdx.x;
   const int per = a.nitems_pad >> 3;
   const int item = (b & 7) * per + (b >> 3);
-  if (item >= a.nitems) return;
+  if (item >= a.nitems) return false;
   int r = 0;
   for (int i = 1; i < a.nreq; ++i)
     if (item >= a.reqs[i].item_base) r = i;
   const ReqDev& rq = a.reqs[r];
   int local = item - rq.item_base;
-  const int rg = local % rq.nrg;
+  *rg = local % rq.nrg;
   local /= rq.nrg;
   const int split = local % rq.nsplit;
   local /= rq.nsplit;
-  const int g = local % a.Hkv;
-  const int l = local / a.Hkv;
-
-  ItemCtx it;
-  it.rq = &rq;
-  it.pool = &a.pools[rq.pool];
-  it.l = l;
-  it.g = g;
-  it.split = split;
+  it->rq = rq;
+  it->pool = a.pools[rq.pool];
+  it->g = local % a.Hkv;
+  it->l = local / a.Hkv;
+  it->split = split;
   const int ctx_pages = (rq.ctx_len + kBlock - 1) / kBlock;
-  it.p_lo = split * rq.chunk_pages;
-  it.nctx = max(0, min(ctx_pages, it.p_lo + rq.chunk_pages) - it.p_lo);
-  it.nbk = (split == rq.nsplit - 1) ? (rq.q0 + rq.rows + kBlock - 1) / kBlock : 0;
-  it.npages = it.nctx + it.nbk;
-  it.rows_total = rq.rows * a.G;
+  it->p_lo = split * rq.chunk_pages;
+  it->nctx = max(0, min(ctx_pages, it->p_lo + rq.chunk_pages) - it->p_lo);
+  it->nbk = (split == rq.nsplit - 1) ? (rq.q0 + rq.rows + kBlock - 1) / kBlock : 0;
+  it->npages = it->nctx + it->nbk;
+  it->rows_total = rq.rows * a.G;
+  return true;
+}
 
-  if (MODE != 1 && rq.kind == VC_VERIFY) {
-    verify_item<D>(a, it, rg, smem);
-  } else if (MODE != 0) {
-    const int bits = it.pool->bits;
-    if (bits == 16) draft_item<D, 16>(a, it, smem);
-    else if (bits == 2) draft_item<D, 2>(a, it, smem);
-    else draft_item<D, 4>(a, it, smem);
-  }
+template <int D, int NW>
+__device__ __forceinline__ void draft_dispatch(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
+  const int bits = it.pool.bits;
+  if (bits == 16) draft_bf16_item<D, NW, (NW <= 4 ? 4 : 2)>(a, it, smem);
+  else if (bits == 2) draft_item<D, 2, NW>(a, it, smem);
+  else draft_item<D, 4, NW>(a, it, smem);
+}
+
+// Verify items only: 8 waves, one work-group per CU (the ring takes most of the LDS).
+template <int D>
+__global__ __launch_bounds__(kVThreads) void verify_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[VRing<D>::kBytes];
+  ItemCtx it;
+  int rg;
+  if (!decode_item(a, &it, &rg)) return;
+  verify_item<D>(a, it, rg, smem);
+}
+
+// Draft items only, one pool (so one bit width) per launch: 4 waves that split the item's keys.
+template <int D>
+__global__ __launch_bounds__(kDThreads) void draft_bf16_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DRing<D>::kBytes];
+  ItemCtx it;
+  int rg;
+  if (!decode_item(a, &it, &rg)) return;
+  draft_bf16_item<D, kDWaves, 4>(a, it, smem);
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kDThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void draft_kivi_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DraftSmem<D>::kBytes];
+  ItemCtx it;
+  int rg;
+  if (!decode_item(a, &it, &rg)) return;
+  draft_item<D, BITS, kDWaves>(a, it, smem);
+}
+
+// One launch over a mixed list (drafting and verifying requests of a batch together).
+template <int D>
+__global__ __launch_bounds__(kVThreads) void mixed_kernel(const AttnArgs a) {
+  constexpr int kBytes = VRing<D>::kBytes > DRing<D>::kBytes ? VRing<D>::kBytes : DRing<D>::kBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes];
+  ItemCtx it;
+  int rg;
+  if (!decode_item(a, &it, &rg)) return;
+  if (it.rq.kind == VC_VERIFY) verify_item<D>(a, it, rg, smem);
+  else draft_dispatch<D, kVWaves>(a, it, smem);
 }
 
 // Combine split partials: one work-group per (request, layer, kv head) with nsplit > 1.
@@ -688,7 +1019,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
       lsum += f * base[s * sstride + D + 1];
       o += f * *reinterpret_cast<const f32x4*>(base + s * sstride + 4 * cq);
     }
-    o *= 1.f / lsum;
+    o *= lsum > 0.f ? 1.f / lsum : 0.f;
     const int tok = row / a.G, jh = row % a.G;
     float* dst = a.out + ((((int64_t)rq.slot * a.L + l) * a.xmax + rq.q0 + tok) * a.Hq + g * a.G + jh) * D;
     *reinterpret_cast<f32x4*>(dst + 4 * cq) = o;
@@ -699,18 +1030,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
 
 int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_t stream) {
   if (plan.nitems == 0) return VC_OK;
-  dim3 grid(args.nitems_pad), block(kThreads);
+  const dim3 grid(args.nitems_pad);
   bool has_v = false, has_d = false;
   for (int i = 0; i < args.nreq; ++i) (args.reqs[i].kind == VC_VERIFY ? has_v : has_d) = true;
-  const int mode = has_v && has_d ? 2 : (has_v ? 0 : 1);
   if (head_dim == 128) {
-    if (mode == 0) hipLaunchKernelGGL((attn_kernel<128, 0>), grid, block, 0, stream, args);
-    else if (mode == 1) hipLaunchKernelGGL((attn_kernel<128, 1>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((attn_kernel<128, 2>), grid, block, 0, stream, args);
+    if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
+    else if (has_v) hipLaunchKernelGGL(verify_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
+    else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<128>, grid, dim3(kDThreads), 0, stream, args);
+    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<128, 2>), grid, dim3(kDThreads), 0, stream, args);
+    else hipLaunchKernelGGL((draft_kivi_kernel<128, 4>), grid, dim3(kDThreads), 0, stream, args);
   } else {
-    if (mode == 0) hipLaunchKernelGGL((attn_kernel<64, 0>), grid, block, 0, stream, args);
-    else if (mode == 1) hipLaunchKernelGGL((attn_kernel<64, 1>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((attn_kernel<64, 2>), grid, block, 0, stream, args);
+    if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
+    else if (has_v) hipLaunchKernelGGL(verify_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
+    else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<64>, grid, dim3(kDThreads), 0, stream, args);
+    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<64, 2>), grid, dim3(kDThreads), 0, stream, args);
+    else hipLaunchKernelGGL((draft_kivi_kernel<64, 4>), grid, dim3(kDThreads), 0, stream, args);
   }
   int rc = hip_check(hipGetLastError(), "attention launch");
   if (rc) return rc;

@@ -77,4 +77,21 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
 
 int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_t stream);
 
+// Context pages of one work item are capped so that their block ids fit the kernels' LDS.
+constexpr int kMaxChunkPages = 2048;
+
+// Split of one request's context into chunks of at most `target` pages (a multiple of 4), with
+// the chunks made as even as possible: returns the chunk size and sets *nsplit.
+inline int split_context(int pages, int target, int* nsplit) {
+  if (pages <= 0) {
+    *nsplit = 1;
+    return target;
+  }
+  const int n = (pages + target - 1) / target;
+  int chunk = (pages + n - 1) / n;
+  chunk = (chunk + 3) / 4 * 4;
+  *nsplit = (pages + chunk - 1) / chunk;
+  return chunk;
+}
+
 }  // namespace vc
