@@ -40,7 +40,7 @@ static int check_shape(const vc_shape* s) {
   return VC_OK;
 }
 
-static int check_pool(const vc_pool* p, int head_dim, const char* name) {
+static int check_pool(const vc_pool* p, int head_dim, int num_layers, int num_kv_heads, const char* name) {
   char buf[160];
   if (!p) {
     snprintf(buf, sizeof buf, "%s pool is NULL", name);
@@ -61,6 +61,11 @@ static int check_pool(const vc_pool* p, int head_dim, const char* name) {
   if (p->num_blocks < 1 || p->max_pages < 1) {
     snprintf(buf, sizeof buf, "%s pool: num_blocks and max_pages must be >= 1", name);
     return fail(VC_EINVAL, buf);
+  }
+  // the kernels index (layer, block, kv head) page units with 32-bit integers
+  if ((int64_t)num_layers * p->num_blocks * num_kv_heads >= (1LL << 31)) {
+    snprintf(buf, sizeof buf, "%s pool: layers x blocks x kv heads must be below 2^31", name);
+    return fail(VC_EUNSUPPORTED, buf);
   }
   (void)head_dim;
   return VC_OK;
@@ -131,7 +136,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
     }
     const vc_pool& p = pools[r.pool];
     if (!pool_used[r.pool]) {
-      rc = check_pool(&p, D, "attention");
+      rc = check_pool(&p, D, s->num_layers, s->num_kv_heads, "attention");
       if (rc) return rc;
       pool_used[r.pool] = 1;
     }

@@ -20,6 +20,8 @@
 // workspace and a merge kernel combines them with log-sum-exp weights.
 #include <math.h>
 
+#include <type_traits>
+
 #include "vc_internal.h"
 
 namespace vc {
@@ -198,26 +200,35 @@ __device__ __forceinline__ int swz_k(int key) {
 // ------------------------------------------------------------------ verify path (32x32x16)
 // A verify work-group has 8 waves: wave w owns row block w & 3 (32 query rows) and key half
 // w >> 2 of every 64-key tile.  K/V pages move from HBM straight into a 4-stage LDS ring with
-// gfx950's global_load_lds_dwordx4 (no register staging), three tiles ahead of the one being
-// consumed; each wave moves one 4 KB page of every tile (waves 0-3 keys, 4-7 values), so each
-// wave's vmcnt counts its own share of the ring.  The two key halves of a row block are merged
-// through LDS at the end.
+// gfx950's global_load_lds_dwordx4 (no register staging); each wave moves one 4 KB page of every
+// tile (waves 0-3 keys, 4-7 values), so each wave's vmcnt counts its own share of the ring.
+// Keys run one tile ahead of values: the scores of tile t + 1 (MFMA) are computed while the
+// softmax of tile t (VALU) runs.  The two key halves of a row block are merged through LDS at
+// the end.
 constexpr int kVWaves = 8;
 constexpr int kVThreads = 64 * kVWaves;
 constexpr int kVStages = 4;
 
+// LDS: the 4 key stages, then the 4 value stages, then the page units of the item.  With the
+// key stages in the first 64 KB, every ring read is an invariant per-lane offset plus a 16-bit
+// immediate once the stage is known at compile time.
 template <int D>
 struct VRing {
   static constexpr int kPage = kBlock * D * 2;      // bytes of one K or V page
-  static constexpr int kTileK = 4 * kPage;          // 64 keys
-  static constexpr int kStage = 2 * kTileK;         // keys then values
-  static constexpr int kRing = kVStages * kStage;
-  static constexpr int kIds = kRing;                // LDS offset of the page ids
-  static constexpr int kBytes = kRing + kMaxChunkPages * 4;
+  static constexpr int kTileK = 4 * kPage;          // one stage: 64 keys (or their values)
+  static constexpr int kV0 = kVStages * kTileK;     // offset of the value stages
+  static constexpr int kRing = 2 * kV0;
+  static constexpr int kIds = kRing;                // LDS offset of the page units
+  static constexpr int kBytes = kRing + kMaxChunkPages * 4 + 16;
   static constexpr int kLoads = kPage / 1024;       // 16-byte-per-lane loads per wave per tile
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Cache policy of the ring loads: nontemporal ("nt").  K/V pages are read exactly once, and
+// streaming them without it leaves chip-wide HBM throughput near 6.3 TB/s instead of about
+// 7.2 TB/s on an MI355X.
+constexpr int kNontemporal = 2;
 
 // wait until at most N (< 64) of this wave's vector memory loads are outstanding (loads
 // complete in issue order).  gfx9 s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] and
@@ -269,191 +280,313 @@ __device__ __forceinline__ bool vkey_visible(const VPage& p, int tt, int qpos) {
   return tt < p.valid && (p.kind == 0 || p.bpos + tt <= qpos);
 }
 
-// Issue this wave's share of tile `t` into ring stage t % 4: one K page (waves 0-3) or one V
-// page (waves 4-7).  A missing page reads block 0 of the pool (always in bounds) and is masked
-// when consumed, so every wave issues the same number of loads per tile.  The K and V cases are
-// separate code paths: choosing between the descriptor fields by reference would make the
-// compiler copy the whole kernel argument block to scratch.
-template <int D, bool V>
-__device__ __forceinline__ void verify_issue_kv(const uint8_t* pool_base, const uint16_t* blk,
-                                                const AttnArgs& a, const ItemCtx& it,
-                                                const int32_t* ids, uint8_t* smem, int t, int ps,
-                                                int lane) {
-  using R = VRing<D>;
-  const int ip = 4 * t + ps;
-  const uint8_t* page;
-  if (ip < it.nctx || ip >= it.npages) {
-    int phys = ip < it.nctx ? ids[ip] : 0;
-    if (phys < 0) phys = 0;
-    page = pool_base + (((int64_t)it.l * it.pool.nblk + phys) * a.Hkv + it.g) * R::kPage;
-  } else {
-    const int64_t unit = (((int64_t)it.rq.slot * a.L + it.l) * a.Hkv + it.g) * (a.xmax / kBlock) +
-                         (ip - it.nctx);
-    page = reinterpret_cast<const uint8_t*>(blk) + unit * R::kPage;
+// Max / sum with the lane 32 positions away (the other half of a 32x32 MFMA column), on the
+// VALU: v_permlane32_swap exchanges the two 32-lane halves of its operands, so with both
+// operands equal to x each lane ends up holding its own value and its partner's.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Everything a verify work item keeps across its tiles.
+template <int D>
+struct VerifyState {
+  static constexpr int NS = D / 16;  // MFMA k-steps of the score product
+  static constexpr int ND = D / 32;  // 32-wide d blocks of the output
+  static constexpr int NL = VRing<D>::kLoads;
+  const int32_t* units;   // LDS: unit index of each context page of the item, -1 if invalid
+  int64_t dummy_unit;     // block 0 of this (layer, kv head): a readable page for missing ones
+  int64_t blk_unit0;      // drafted-block page 0 of this (request, layer, kv head)
+  int ntiles, t_full;
+  int ps;                 // page of every tile this wave loads
+  bool kwave;             // loads keys (waves 0-3) or values (4-7)
+  bool wave_on;           // the wave's row block holds rows
+  int kh, n, h, qpos;
+  uint32_t lane_off[NL];  // byte offsets inside a page of this lane's loads
+  uint32_t koff[NS];      // LDS offsets (inside a key stage) of this lane's score operands
+  uint32_t voff;          // LDS offset of this lane's value operand (stage 0, page 2 kh, d block 0)
+  u32x4 qreg[NS];         // query rows: B operand of S^T = K Q^T
+  f32x16 acc_o[ND];
+  float m_run, l_run, sc;
+};
+
+// Global address of page `ip` of the item (scalar): a context page (its unit, or the dummy when
+// the table entry is invalid), a drafted-block page, or the dummy past the item's pages.
+template <int D>
+__device__ __forceinline__ const uint8_t* verify_page(const uint8_t* pool_base, const uint16_t* blk,
+                                                      const ItemCtx& it, const VerifyState<D>& vs, int ip) {
+  constexpr int P = VRing<D>::kPage;
+  if (ip < it.nctx) {
+    const int u = __builtin_amdgcn_readfirstlane(vs.units[ip]);
+    return pool_base + (u >= 0 ? (int64_t)u : vs.dummy_unit) * P;
   }
-  uint8_t* dst = smem + (t & (kVStages - 1)) * R::kStage + (V ? R::kTileK : 0) + ps * R::kPage;
+  if (ip < it.npages) return reinterpret_cast<const uint8_t*>(blk) + (vs.blk_unit0 + (ip - it.nctx)) * P;
+  return pool_base + vs.dummy_unit * P;
+}
+
+// Issue this wave's page of tile t into ring stage `stage`.  Every wave issues the same number
+// of loads per tile (a missing page reads the dummy and is masked when consumed), so vmcnt
+// counts are exact.
+template <int D>
+__device__ __forceinline__ void verify_issue(const AttnArgs& a, const ItemCtx& it, const VerifyState<D>& vs,
+                                             uint8_t* smem, int t, int stage) {
+  using R = VRing<D>;
+  const int ip = 4 * t + vs.ps;
+  // K and V are separate calls: choosing between descriptor fields by reference would make
+  // the compiler copy the kernel argument block to scratch
+  const uint8_t* page = vs.kwave ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip)
+                                 : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip);
+  uint8_t* dst = smem + (vs.kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;
 #pragma unroll
   for (int i = 0; i < R::kLoads; ++i) {
-    int off;
-    if constexpr (!V) {
-      constexpr int CPR = D / 8;           // 16-byte chunks per key row
-      constexpr int RPI = 1024 / (2 * D);  // key rows per load
-      const int tok = RPI * i + lane / CPR, slot = lane % CPR;
-      off = tok * (2 * D) + ((slot ^ swz_k<D>(tok)) * 16);
-    } else {
-      const int dd = 32 * i + (lane >> 1), slot = lane & 1;
-      off = dd * 32 + ((slot ^ ((dd >> 3) & 1)) * 16);
-    }
-    __builtin_amdgcn_global_load_lds(page + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
+    const void* src = page + vs.lane_off[i];
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, kNontemporal);
   }
 }
 
+// wait until at most `tiles` of this wave's ring tiles are in flight
 template <int D>
-__device__ __forceinline__ void verify_issue(const AttnArgs& a, const ItemCtx& it, const int32_t* ids,
-                                             uint8_t* smem, int t, int w, int lane) {
-  if (w < 4) verify_issue_kv<D, false>(it.pool.k, a.blk_k, a, it, ids, smem, t, w & 3, lane);
-  else verify_issue_kv<D, true>(it.pool.v, a.blk_v, a, it, ids, smem, t, w & 3, lane);
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  constexpr int L = VRing<D>::kLoads;
+  if (tiles >= 3) wait_vmem<3 * L>();
+  else if (tiles == 2) wait_vmem<2 * L>();
+  else if (tiles == 1) wait_vmem<L>();
+  else wait_vmem<0>();
+}
+
+// S^T for this wave's 32 keys (key half kh) of the tile in key stage `st`
+template <int D>
+__device__ __forceinline__ f32x16 verify_scores(const uint8_t* smem, int st, const VerifyState<D>& vs) {
+  using R = VRing<D>;
+  f32x16 acc = f32x16{};
+  const uint8_t* kst = smem + st * R::kTileK;
+#pragma unroll
+  for (int s = 0; s < VerifyState<D>::NS; ++s) {
+    const u32x4 av = ld16(kst + vs.koff[s]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(vs.qreg[s]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Online softmax of one tile's scores and O^T += V^T P^T from value stage `st`.  MASK: the tile
+// holds a partial, missing or drafted-block page (per-key visibility and value masking);
+// otherwise every key of the tile is a visible context key.
+template <int D, bool MASK>
+__device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>& vs, const uint8_t* smem,
+                                               int t, int st, f32x16 s_acc) {
+  using R = VRing<D>;
+  constexpr int ND = VerifyState<D>::ND;
+  const int h = vs.h;
+  VPage p0, p1;
+  if constexpr (MASK) {
+    p0 = vpage_info(it, vs.units, 4 * t + 2 * vs.kh);
+    p1 = vpage_info(it, vs.units, 4 * t + 2 * vs.kh + 1);
+    // register r holds key (page 2 kh + r / 8, token 8 h + r % 8) of row n
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!vkey_visible(r < 8 ? p0 : p1, 8 * h + (r & 7), vs.qpos)) s_acc[r] = -INFINITY;
+  }
+  float mloc = fmaxf(fmaxf(fmaxf(s_acc[0], s_acc[1]), fmaxf(s_acc[2], s_acc[3])),
+                     fmaxf(fmaxf(s_acc[4], s_acc[5]), fmaxf(s_acc[6], s_acc[7])));
+  mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s_acc[8], s_acc[9]), fmaxf(s_acc[10], s_acc[11])),
+                           fmaxf(fmaxf(s_acc[12], s_acc[13]), fmaxf(s_acc[14], s_acc[15]))));
+  mloc = half_swap_max(mloc);
+  const float sc = vs.sc;
+  const float m_new = fmaxf(vs.m_run, mloc * sc);
+  if (__any(m_new > vs.m_run + kLazyRescale)) {
+    const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
+    vs.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) vs.acc_o[i] *= alpha;
+    vs.m_run = m_new;
+  }
+  const float m_use = (vs.m_run == -INFINITY) ? 0.f : vs.m_run;
+  uint32_t pb[8];
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s_acc[r], sc, -m_use));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s_acc[r + 1], sc, -m_use));
+    ls0 += e0;
+    ls1 += e1;
+    pb[r >> 1] = pack_bf16(e0, e1);
+  }
+  vs.l_run += ls0 + ls1;
+  const uint8_t* vst = smem + st * R::kTileK + vs.voff;
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj) {
+    const u32x4 bv = {pb[4 * pj], pb[4 * pj + 1], pb[4 * pj + 2], pb[4 * pj + 3]};
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      u32x4 av = ld16(vst + pj * R::kPage + db * 1024);
+      if constexpr (MASK) av = mask_tokens(av, 8 * h, (pj ? p1 : p0).valid);
+      vs.acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(bv), vs.acc_o[db], 0, 0, 0);
+    }
+  }
+}
+
+// One tile: wait for K(t + 1) (key waves) / V(t) (value waves), refill the dead stages (K(t + 4)
+// into key stage t % 4, V(t + 3) into value stage (t - 1) % 4), score tile t + 1 into s_nxt (the
+// last tile scores a stale stage, unused) and consume tile t.  STC >= 0: t % 4 == STC known at
+// compile time.
+template <int D, int STC, bool MASK>
+__device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs,
+                                            uint8_t* smem, int t, f32x16& s_cur, f32x16& s_nxt) {
+  const int st = STC >= 0 ? STC : (t & (kVStages - 1));
+  const int ntiles = vs.ntiles;
+  if (vs.kwave) {
+    if (t + 1 < ntiles) wait_tiles<D>(min(2, ntiles - t - 2));
+  } else {
+    wait_tiles<D>(min(2, ntiles - t - 1));
+  }
+  ring_barrier();
+  if (vs.kwave) {
+    if (t + kVStages < ntiles) verify_issue<D>(a, it, vs, smem, t + kVStages, st);
+  } else {
+    if (t + kVStages - 1 < ntiles) verify_issue<D>(a, it, vs, smem, t + kVStages - 1, (st + kVStages - 1) & (kVStages - 1));
+  }
+  if (!vs.wave_on) return;
+  s_nxt = verify_scores<D>(smem, (st + 1) & (kVStages - 1), vs);
+  verify_consume<D, MASK>(it, vs, smem, t, st, s_cur);
 }
 
 template <int D>
 __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
   using R = VRing<D>;
-  constexpr int NS = D / 16;  // MFMA k-steps of the score product
-  constexpr int ND = D / 32;  // 32-wide d blocks of the output
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const int rb = w & 3, kh = w >> 2;
+  using VS = VerifyState<D>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int rb = w & 3;
   const ReqDev& rq = it.rq;
   const int G = a.G;
   const int row = rg * 128 + 32 * rb + n;
-  const bool wave_on = rg * 128 + 32 * rb < it.rows_total;
   const bool row_ok = row < it.rows_total;
   const int tok = row_ok ? row / G : 0;
-  const int qpos = rq.q0 + tok;
 
-  // query rows as the B operand of S^T = K Q^T
-  u32x4 qreg[NS];
+  VS vs;
+  vs.kh = w >> 2;
+  vs.n = n;
+  vs.h = h;
+  vs.kwave = w < 4;
+  vs.ps = w & 3;
+  vs.wave_on = rg * 128 + 32 * rb < it.rows_total;
+  vs.qpos = rq.q0 + tok;
+  vs.sc = a.scale_log2;
   {
     const uint16_t* qp = a.q + ((((int64_t)rq.slot * a.L + it.l) * a.xmax + rq.q0 + tok) * a.Hq +
                                 it.g * G + (row_ok ? row % G : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qreg[s] = row_ok ? ld16(qp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < VS::NS; ++s) vs.qreg[s] = row_ok ? ld16(qp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
   }
 
-  // block ids of this item's context pages (invalid entries become -1)
-  int32_t* ids = reinterpret_cast<int32_t*>(smem + R::kIds);
+  // unit index of every context page of the item, and the first invalid one
+  int32_t* units = reinterpret_cast<int32_t*>(smem + R::kIds);
+  int* first_bad = units + kMaxChunkPages;
   {
     const PoolDev& pl = it.pool;
+    vs.dummy_unit = (int64_t)it.l * pl.nblk * a.Hkv + it.g;
+    vs.blk_unit0 = (((int64_t)rq.slot * a.L + it.l) * a.Hkv + it.g) * (a.xmax / kBlock);
+    if (tid == 0) *first_bad = it.nctx;
+    __syncthreads();
     const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
     for (int i = tid; i < it.nctx; i += kVThreads) {
       const int phys = pt[i];
-      ids[i] = (phys < 0 || phys >= pl.nblk) ? -1 : phys;
+      const bool ok = phys >= 0 && phys < pl.nblk;
+      units[i] = ok ? (int32_t)(vs.dummy_unit + (int64_t)phys * a.Hkv) : -1;
+      if (!ok) atomicMin(first_bad, i);
     }
   }
-  // the query registers and page ids are complete before the first ring load is issued, so the
-  // loop's vmcnt waits cover ring loads only
+  // the query registers and page table reads are complete before the first ring load is
+  // issued, so the loop's vmcnt waits cover ring loads only
   wait_vmem<0>();
   __syncthreads();
+  vs.units = units;
+  vs.ntiles = (it.npages + 3) >> 2;
+  const int ntiles = vs.ntiles;
+  const int nfull = min(it.nctx, max(0, (rq.ctx_len - kBlock * it.p_lo) / kBlock));
+  vs.t_full = min(nfull, *first_bad) >> 2;  // leading tiles of 4 full, valid context pages
 
-  const int ntiles = (it.npages + 3) >> 2;
+  // Per-lane offsets.  Loads: the LDS side of global_load_lds is lane-linear, so the XOR
+  // swizzle of the ring is applied by choosing which global chunk each lane fetches.
 #pragma unroll
-  for (int t = 0; t < kVStages - 1; ++t)
-    if (t < ntiles) verify_issue<D>(a, it, ids, smem, t, w, lane);
+  for (int i = 0; i < VS::NL; ++i) {
+    if (vs.kwave) {
+      constexpr int CPR = D / 8;           // 16-byte chunks per key row
+      constexpr int RPI = 1024 / (2 * D);  // key rows per load
+      const int tk = RPI * i + lane / CPR, sl = lane % CPR;
+      vs.lane_off[i] = tk * (2 * D) + ((sl ^ swz_k<D>(tk)) * 16);
+    } else {
+      const int dd = 32 * i + (lane >> 1), sl = lane & 1;
+      vs.lane_off[i] = dd * 32 + ((sl ^ ((dd >> 3) & 1)) * 16);
+    }
+  }
+  {
+    const int key = 32 * vs.kh + key_of_m32(n);
+    const int ksw = swz_k<D>(key);
+#pragma unroll
+    for (int s = 0; s < VS::NS; ++s) vs.koff[s] = key * (2 * D) + (((2 * s + h) ^ ksw) * 16);
+    vs.voff = R::kV0 + 2 * vs.kh * R::kPage + n * 32 + ((h ^ ((n >> 3) & 1)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VS::ND; ++i) vs.acc_o[i] = f32x16{};
+  vs.m_run = -INFINITY;
+  vs.l_run = 0.f;
 
-  f32x16 acc_o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) acc_o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sc = a.scale_log2;
-  const int key = 32 * kh + key_of_m32(n);
-  const int ksw = swz_k<D>(key);
+  // prologue: K(0..3), V(0..2); scores of tile 0
+  const int kpro = min(ntiles, kVStages), vpro = min(ntiles, kVStages - 1);
+  for (int j = 0; j < (vs.kwave ? kpro : vpro); ++j) verify_issue<D>(a, it, vs, smem, j, j);
+  if (vs.kwave) wait_tiles<D>(kpro - 1);  // K(0)
+  ring_barrier();
+  f32x16 s_a = vs.wave_on ? verify_scores<D>(smem, 0, vs) : f32x16{};
+  f32x16 s_b = f32x16{};
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int ahead = min(kVStages - 2, ntiles - 1 - t);  // tiles issued after t
-    if (ahead >= 2) wait_vmem<2 * R::kLoads>();
-    else if (ahead == 1) wait_vmem<R::kLoads>();
-    else wait_vmem<0>();
-    ring_barrier();  // tile t is in LDS for every wave; stage (t - 1) is free
-    if (t + kVStages - 1 < ntiles) verify_issue<D>(a, it, ids, smem, t + kVStages - 1, w, lane);
-    if (!wave_on) continue;
-
-    const uint8_t* sk = smem + (t & (kVStages - 1)) * R::kStage;
-    const uint8_t* sv = sk + R::kTileK;
-    f32x16 s_acc = f32x16{};
-    const uint8_t* krow = sk + key * (2 * D);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const u32x4 av = ld16(krow + (((2 * s + h) ^ ksw) * 16));
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(qreg[s]), s_acc, 0, 0, 0);
-    }
-    // register r holds key (page 2*kh + r/8, token 8h + r%8) of row n
-    const VPage p0 = vpage_info(it, ids, 4 * t + 2 * kh);
-    const VPage p1 = vpage_info(it, ids, 4 * t + 2 * kh + 1);
-    const bool full = p0.kind == 0 && p0.valid == kBlock && p1.kind == 0 && p1.valid == kBlock;
-    if (!full) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!vkey_visible(r < 8 ? p0 : p1, 8 * h + (r & 7), qpos)) s_acc[r] = -INFINITY;
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s_acc[r]);
-    mloc = wave_xor_max(mloc, 32);
-    const float m_new = fmaxf(m_run, mloc * sc);
-    if (__any(m_new > m_run + kLazyRescale)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    uint32_t pb[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(s_acc[r], sc, -m_use));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(s_acc[r + 1], sc, -m_use));
-      l_run += e0 + e1;
-      pb[r >> 1] = pack_bf16(e0, e1);
-    }
-    // O^T += V^T P^T, one page (16 keys) per k-step
-#pragma unroll
-    for (int pj = 0; pj < 2; ++pj) {
-      const u32x4 bv = {pb[4 * pj], pb[4 * pj + 1], pb[4 * pj + 2], pb[4 * pj + 3]};
-      const VPage& pp = pj ? p1 : p0;
-      const uint8_t* vpg = sv + (2 * kh + pj) * (D * 32);
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int dd = 32 * db + n;
-        u32x4 av = ld16(vpg + dd * 32 + ((h ^ ((dd >> 3) & 1)) * 16));
-        if (!full && !(pp.kind == 0 && pp.valid == kBlock)) av = mask_tokens(av, 8 * h, pp.valid);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(bv), acc_o[db], 0, 0, 0);
-      }
-    }
+  // full tiles (no masking) four at a time, so ring stages are compile-time and the scores
+  // alternate between s_a and s_b without register copies; then the rest, with masking
+  int t = 0;
+  for (; t + 3 < vs.t_full; t += 4) {
+    verify_step<D, 0, false>(a, it, vs, smem, t, s_a, s_b);
+    verify_step<D, 1, false>(a, it, vs, smem, t + 1, s_b, s_a);
+    verify_step<D, 2, false>(a, it, vs, smem, t + 2, s_a, s_b);
+    verify_step<D, 3, false>(a, it, vs, smem, t + 3, s_b, s_a);
+  }
+  for (; t < vs.t_full; ++t) {
+    verify_step<D, -1, false>(a, it, vs, smem, t, s_a, s_b);
+    s_a = s_b;
+  }
+  for (; t < ntiles; ++t) {
+    verify_step<D, -1, true>(a, it, vs, smem, t, s_a, s_b);
+    s_a = s_b;
   }
 
   // merge the two key halves of every row block through LDS (the ring is free now)
   __syncthreads();
+  constexpr int ND = VS::ND;
   constexpr int NR = ND * 16;  // accumulator floats per lane
   float* red = reinterpret_cast<float*>(smem) + rb * (64 * (NR + 2));
-  if (kh == 1 && wave_on) {
+  if (vs.kh == 1 && vs.wave_on) {
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(red + ((db * 4 + q) * 64 + lane) * 4) =
-            f32x4{acc_o[db][4 * q], acc_o[db][4 * q + 1], acc_o[db][4 * q + 2], acc_o[db][4 * q + 3]};
-    red[NR * 64 + lane] = m_run;
-    red[NR * 64 + 64 + lane] = l_run;
+            f32x4{vs.acc_o[db][4 * q], vs.acc_o[db][4 * q + 1], vs.acc_o[db][4 * q + 2], vs.acc_o[db][4 * q + 3]};
+    red[NR * 64 + lane] = vs.m_run;
+    red[NR * 64 + 64 + lane] = vs.l_run;
   }
   __syncthreads();
-  if (kh == 1 || !wave_on) return;
+  if (vs.kh == 1 || !vs.wave_on) return;
   const float m1 = red[NR * 64 + lane], l1 = red[NR * 64 + 64 + lane];
-  const float M = fmaxf(m_run, m1);
-  const float f0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  const float M = fmaxf(vs.m_run, m1);
+  const float f0 = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - M);
   const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-  const float l_tot = wave_xor_sum(f0 * l_run + f1 * l1, 32);
+  const float l_tot = half_swap_sum(f0 * vs.l_run + f1 * l1);
   if (!row_ok) return;
   bool partial;
   float* dst = out_row<D>(a, it, row, &partial);
@@ -463,7 +596,7 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 o1 = *reinterpret_cast<const f32x4*>(red + ((db * 4 + q) * 64 + lane) * 4);
-      f32x4 o = {acc_o[db][4 * q], acc_o[db][4 * q + 1], acc_o[db][4 * q + 2], acc_o[db][4 * q + 3]};
+      f32x4 o = {vs.acc_o[db][4 * q], vs.acc_o[db][4 * q + 1], vs.acc_o[db][4 * q + 2], vs.acc_o[db][4 * q + 3]};
       o = (f0 * o + f1 * o1) * inv;
       *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q + 4 * h) = o;
     }
@@ -583,7 +716,7 @@ __device__ __forceinline__ void draft_issue_kv(const uint8_t* pool_base, const u
       const int dd = 32 * i + (lane >> 1), s = lane & 1;
       off = dd * 32 + ((s ^ ((dd >> 2) & 1)) * 16);
     }
-    __builtin_amdgcn_global_load_lds(page + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(page + off, (lds_ptr_t)(dst + i * 1024), 16, 0, kNontemporal);
   }
 }
 
