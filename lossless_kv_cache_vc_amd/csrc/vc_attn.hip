@@ -207,17 +207,18 @@ __device__ __forceinline__ int swz_k(int key) {
 // the end.
 constexpr int kVWaves = 8;
 constexpr int kVThreads = 64 * kVWaves;
-constexpr int kVStages = 4;
+constexpr int kVStages = 4;   // key stages (keys are loaded 4 tiles ahead)
+constexpr int kVVStages = 5;  // value stages (values are loaded 4 tiles ahead, consumed a tile later)
 
-// LDS: the 4 key stages, then the 4 value stages, then the page units of the item.  With the
-// key stages in the first 64 KB, every ring read is an invariant per-lane offset plus a 16-bit
-// immediate once the stage is known at compile time.
+// LDS: the 4 key stages, then the 5 value stages, then the page units of the item.  With the
+// key stages in the first 64 KB, every key read is an invariant per-lane offset plus a 16-bit
+// immediate once the stage is known at compile time; value reads add one per-tile base.
 template <int D>
 struct VRing {
   static constexpr int kPage = kBlock * D * 2;      // bytes of one K or V page
   static constexpr int kTileK = 4 * kPage;          // one stage: 64 keys (or their values)
   static constexpr int kV0 = kVStages * kTileK;     // offset of the value stages
-  static constexpr int kRing = 2 * kV0;
+  static constexpr int kRing = kV0 + kVVStages * kTileK;
   static constexpr int kIds = kRing;                // LDS offset of the page units
   static constexpr int kBytes = kRing + kMaxChunkPages * 4 + 16;
   static constexpr int kLoads = kPage / 1024;       // 16-byte-per-lane loads per wave per tile
@@ -304,6 +305,8 @@ struct VerifyState {
   int64_t dummy_unit;     // block 0 of this (layer, kv head): a readable page for missing ones
   int64_t blk_unit0;      // drafted-block page 0 of this (request, layer, kv head)
   int ntiles, t_full;
+  int pf_unit;            // unit of the page this wave loads next (read from LDS one tile early)
+  int vst;                // value stage of the tile being consumed (t % 5)
   int ps;                 // page of every tile this wave loads
   bool kwave;             // loads keys (waves 0-3) or values (4-7)
   bool wave_on;           // the wave's row block holds rows
@@ -320,10 +323,11 @@ struct VerifyState {
 // the table entry is invalid), a drafted-block page, or the dummy past the item's pages.
 template <int D>
 __device__ __forceinline__ const uint8_t* verify_page(const uint8_t* pool_base, const uint16_t* blk,
-                                                      const ItemCtx& it, const VerifyState<D>& vs, int ip) {
+                                                      const ItemCtx& it, const VerifyState<D>& vs, int ip,
+                                                      int unit) {
   constexpr int P = VRing<D>::kPage;
   if (ip < it.nctx) {
-    const int u = __builtin_amdgcn_readfirstlane(vs.units[ip]);
+    const int u = __builtin_amdgcn_readfirstlane(unit);
     return pool_base + (u >= 0 ? (int64_t)u : vs.dummy_unit) * P;
   }
   if (ip < it.npages) return reinterpret_cast<const uint8_t*>(blk) + (vs.blk_unit0 + (ip - it.nctx)) * P;
@@ -335,14 +339,14 @@ __device__ __forceinline__ const uint8_t* verify_page(const uint8_t* pool_base, 
 // counts are exact.
 template <int D>
 __device__ __forceinline__ void verify_issue(const AttnArgs& a, const ItemCtx& it, const VerifyState<D>& vs,
-                                             uint8_t* smem, int t, int stage) {
+                                             uint8_t* smem, int t, int stage, int unit) {
   using R = VRing<D>;
   const int ip = 4 * t + vs.ps;
   // K and V are separate calls: choosing between descriptor fields by reference would make
   // the compiler copy the kernel argument block to scratch
-  const uint8_t* page = vs.kwave ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip)
-                                 : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip);
-  uint8_t* dst = smem + (vs.kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;
+  const uint8_t* page = vs.kwave ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip, unit)
+                                 : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip, unit);
+  uint8_t* dst = smem + (vs.kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;  // stage < 4 (K) or < 5 (V)
 #pragma unroll
   for (int i = 0; i < R::kLoads; ++i) {
     const void* src = page + vs.lane_off[i];
@@ -379,7 +383,7 @@ __device__ __forceinline__ f32x16 verify_scores(const uint8_t* smem, int st, con
 // otherwise every key of the tile is a visible context key.
 template <int D, bool MASK>
 __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>& vs, const uint8_t* smem,
-                                               int t, int st, f32x16 s_acc) {
+                                               int t, int vst, f32x16 s_acc) {
   using R = VRing<D>;
   constexpr int ND = VerifyState<D>::ND;
   const int h = vs.h;
@@ -418,13 +422,13 @@ __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>
     pb[r >> 1] = pack_bf16(e0, e1);
   }
   vs.l_run += ls0 + ls1;
-  const uint8_t* vst = smem + st * R::kTileK + vs.voff;
+  const uint8_t* vbase = smem + vst * R::kTileK + vs.voff;
 #pragma unroll
   for (int pj = 0; pj < 2; ++pj) {
     const u32x4 bv = {pb[4 * pj], pb[4 * pj + 1], pb[4 * pj + 2], pb[4 * pj + 3]};
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      u32x4 av = ld16(vst + pj * R::kPage + db * 1024);
+      u32x4 av = ld16(vbase + pj * R::kPage + db * 1024);
       if constexpr (MASK) av = mask_tokens(av, 8 * h, (pj ? p1 : p0).valid);
       vs.acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av), as_bf(bv), vs.acc_o[db], 0, 0, 0);
     }
@@ -440,20 +444,27 @@ __device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it
                                             uint8_t* smem, int t, f32x16& s_cur, f32x16& s_nxt) {
   const int st = STC >= 0 ? STC : (t & (kVStages - 1));
   const int ntiles = vs.ntiles;
+  // keys: K(t + 1) must have landed (K issued up to t + 3); values: V(t) (V issued up to t + 3)
   if (vs.kwave) {
     if (t + 1 < ntiles) wait_tiles<D>(min(2, ntiles - t - 2));
   } else {
-    wait_tiles<D>(min(2, ntiles - t - 1));
+    wait_tiles<D>(min(3, ntiles - t - 1));
   }
   ring_barrier();
-  if (vs.kwave) {
-    if (t + kVStages < ntiles) verify_issue<D>(a, it, vs, smem, t + kVStages, st);
-  } else {
-    if (t + kVStages - 1 < ntiles) verify_issue<D>(a, it, vs, smem, t + kVStages - 1, (st + kVStages - 1) & (kVStages - 1));
+  // K(t + 4) into key stage t % 4 (K(t) was scored last tile), or V(t + 4) into value stage
+  // (t + 4) % 5 (V(t - 1) was consumed last tile), with the page unit read one tile earlier;
+  // then read the unit for the next tile's load
+  const int vst = vs.vst;
+  const int vst4 = vst == 0 ? kVVStages - 1 : vst - 1;  // (t + 4) % 5
+  if (t + 4 < ntiles) verify_issue<D>(a, it, vs, smem, t + 4, vs.kwave ? st : vst4, vs.pf_unit);
+  {
+    const int ipn = 4 * (t + 5) + vs.ps;
+    vs.pf_unit = ipn < it.nctx ? vs.units[ipn] : -1;
   }
+  vs.vst = vst == kVVStages - 1 ? 0 : vst + 1;
   if (!vs.wave_on) return;
   s_nxt = verify_scores<D>(smem, (st + 1) & (kVStages - 1), vs);
-  verify_consume<D, MASK>(it, vs, smem, t, st, s_cur);
+  verify_consume<D, MASK>(it, vs, smem, t, vst, s_cur);
 }
 
 template <int D>
@@ -539,9 +550,17 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
   vs.m_run = -INFINITY;
   vs.l_run = 0.f;
 
-  // prologue: K(0..3), V(0..2); scores of tile 0
-  const int kpro = min(ntiles, kVStages), vpro = min(ntiles, kVStages - 1);
-  for (int j = 0; j < (vs.kwave ? kpro : vpro); ++j) verify_issue<D>(a, it, vs, smem, j, j);
+  // prologue: K(0..3) and V(0..3) into stages 0..3; scores of tile 0
+  const int kpro = min(ntiles, 4);
+  for (int j = 0; j < kpro; ++j) {
+    const int ip = 4 * j + vs.ps;
+    verify_issue<D>(a, it, vs, smem, j, j, ip < it.nctx ? units[ip] : -1);
+  }
+  {
+    const int ipn = 4 * 4 + vs.ps;
+    vs.pf_unit = ipn < it.nctx ? units[ipn] : -1;
+  }
+  vs.vst = 0;
   if (vs.kwave) wait_tiles<D>(kpro - 1);  // K(0)
   ring_barrier();
   f32x16 s_a = vs.wave_on ? verify_scores<D>(smem, 0, vs) : f32x16{};
