@@ -13,7 +13,6 @@ the draft and verify launches divided by their measured time.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -23,34 +22,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 METRIC = "verify+draft attention achieved HBM TB/s (% of peak), Llama-3.1-8B shape 32K"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    p = os.path.join(ROOT, "lossless_kv_cache_vc_amd", "csrc", "vc_attn.hip")
-    h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(kernel: str, launches_per_step: float):
-    """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
-    scaled by a copy-kernel calibration), or None when absent or taken on other kernel code."""
+def measured_traffic(kind: str):
+    """HBM bytes per launch of one attention kernel from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when absent or
+    taken on other kernel code."""
+    from lossless_kv_cache_vc_amd.profiling import attn_source_hash
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != attn_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("bytes_per_launch")
+    k = rec.get("kernels", {}).get(kind)
+    return None if not k else k.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, units: int):
-    """The oracle, untuned, on a bounded sample of the same round, scaled to the whole round."""
+def cpu_baseline(cfg, budget_s: float):
+    """The oracle, untuned, on a bounded sample of the same round, scaled to the whole round:
+    (request, layer, kv head) units of the verify pass plus all x draft steps are timed until
+    about `budget_s` seconds of oracle work have run, plus one instance's logits and accept."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -62,9 +57,9 @@ def cpu_baseline(cfg, units: int):
     from oracle import workload as ow
 
     G, x = cfg.G, cfg.reqs[0].x
-    picks = [(r % cfg.B, (7 * r) % cfg.L, (3 * r) % cfg.Hkv) for r in range(units)]
-    t_units = 0.0
-    for r, l, g in picks:
+    t_units, units = 0.0, 0
+    while t_units < budget_s and units < cfg.B * cfg.L * cfg.Hkv:
+        r, l, g = units % cfg.B, (7 * units) % cfg.L, (3 * units) % cfg.Hkv
         q = ow.queries(cfg, r, l, x)[:, g * G:(g + 1) * G]
         kc, vc = ow.context(cfg, r, l, g)
         kb, vb = ow.block(cfg, r, l, g, x)
@@ -74,6 +69,7 @@ def cpu_baseline(cfg, units: int):
         for i in range(x):
             oatt.draft_unit(q[i], cm.k, cm.v, kb, vb, i)
         t_units += time.perf_counter() - t0
+        units += 1
     t_unit = t_units / units
     wu = np.zeros((cfg.wu_width, cfg.vocab))
     o = np.zeros((x, cfg.Hq * cfg.d))
@@ -87,8 +83,8 @@ def cpu_baseline(cfg, units: int):
     n_inst = cfg.B * cfg.L
     round_s = t_unit * n_units + t_inst * n_inst
     return round_s, threads, (f"{units} (request, layer, kv-head) units of one round (verify pass + "
-                              f"{x} draft steps) and one instance's logits+accept, timed and scaled "
-                              f"by {n_units} units / {n_inst} instances")
+                              f"{x} draft steps; {t_units:.1f} s) and one instance's logits+accept, "
+                              f"timed and scaled by {n_units} units / {n_inst} instances")
 
 
 def main():
@@ -98,11 +94,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle work to time for the CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards "
-              "by request/kv head with no exchange, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: every (request, "
+              "layer, kv head) unit of the path is independent, so more GPUs would each run their "
+              "own share with no exchange", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -155,15 +153,25 @@ def main():
     draft_gbps = (sum(d_bytes) / x) / (draft_launch_ms * 1e-3) / 1e9
     dominant = "draft" if draft_ms >= verify_ms else "verify"
 
+    bits = cfg.reqs[0].bits
+    draft_role = {16: "draft", 2: "draft_kivi2", 4: "draft_kivi4"}[bits]
+    draft_name = {16: "draft_bf16_kernel<128>", 2: "draft_kivi_kernel<128, 2>", 4: "draft_kivi_kernel<128, 4>"}[bits]
+
     def roof(kind):
         if kind == "verify":
-            achieved, per_launch, launches = verify_gbps, v_bytes, 1
+            achieved, per_launch, name, role = verify_gbps, v_bytes, "verify_kernel<128>", "verify"
         else:
-            achieved, per_launch, launches = draft_gbps, sum(d_bytes) / x, x
-        tr = measured_traffic(kind, launches)
+            achieved, per_launch, name, role = draft_gbps, sum(d_bytes) / x, draft_name, draft_role
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": tr,
-                "kernel": f"attn_kernel ({kind} launch)", "algorithmic_bytes_per_launch": int(per_launch)}
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(role),
+                "kernel": name, "algorithmic_bytes_per_launch": int(per_launch)}
+
+    # verify MFMA use: the two bf16 products (scores and weighted values) of every query row
+    # against every key it sees (the whole context plus drafted rows 0..i), 2 flops per
+    # multiply-add
+    v_flops = sum(4 * cfg.G * cfg.d * (r.rows * r.ctx_len + r.rows * (r.rows + 1) // 2)
+                  for r in wl.verify_reqs()) * cfg.L * cfg.Hkv
+    v_tflops = v_flops / (verify_ms * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -187,12 +195,14 @@ def main():
         "pct_of_peak": round(100 * value_tbs * 1e3 / PEAK_HBM_GBPS, 2),
         "roofline": roof(dominant),
         "roofline_verify": roof("verify"),
+        "verify_mfma": {"achieved": round(v_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(v_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": int(v_flops)},
         "breakdown_ms": {"draft_total": round(draft_ms, 3), "draft_per_launch": round(draft_launch_ms, 4),
                          "verify": round(verify_ms, 3), "logits_accept": round(tail_ms, 3)},
         "bytes": {"verify": v_bytes, "draft_per_step_avg": int(sum(d_bytes) / x), "round": round_bytes},
     }
     if not args.no_cpu_baseline:
-        round_s, threads, sample = cpu_baseline(cfg, args.cpu_units)
+        round_s, threads, sample = cpu_baseline(cfg, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(round_bytes / round_s / 1e12, 8), "unit": "TB/s",
                                "cores": threads, "kind": "oracle", "sample": sample,
                                "round_seconds_scaled": round(round_s, 1)}

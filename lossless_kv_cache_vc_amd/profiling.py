@@ -1,0 +1,169 @@
+"""Turn rocprofv3 output into the short summaries kept under ``profiles/``.
+
+Measurement tooling only (it reads CSV files; it launches nothing on the GPU).
+
+* ``stats``   — per-kernel average duration from ``--kernel-trace --stats -f csv`` output.
+* ``traffic`` — HBM bytes per launch of the attention kernels from two ``--pmc`` runs
+  (``FETCH_SIZE``, then ``WRITE_SIZE``, KiB per dispatch), each scaled by what the same counter
+  reads for a plain device copy of known size (``copy_probe.py``).  The result is written as
+  JSON together with a hash of the attention source, so a later change to the kernels makes the
+  stored traffic stale (the benchmark then reports ``null``).
+* ``sq``      — instruction and MFMA counters of the verify kernel (utilisation figures).
+
+    python -m lossless_kv_cache_vc_amd.profiling stats --csv DIR/x_kernel_stats.csv --out profiles/a.md --cmd "..."
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+from typing import Dict, List
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ATTN_SRC = os.path.join(PKG, "csrc", "vc_attn.hip")
+
+# kernel-name fragment -> role reported by the benchmark
+ROLES = {
+    "verify_kernel<128>": "verify",
+    "draft_bf16_kernel<128>": "draft",
+    "draft_kivi_kernel<128, 2>": "draft_kivi2",
+    "draft_kivi_kernel<128, 4>": "draft_kivi4",
+    "mixed_kernel<128>": "mixed",
+    "merge_kernel<128>": "merge",
+}
+
+
+def attn_source_hash() -> str:
+    """Short hash of the attention kernels' source (stored traffic is valid only for it)."""
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _role(name: str):
+    for frag, role in ROLES.items():
+        if frag in name:
+            return role
+    return None
+
+
+def _counters(path_glob: str) -> Dict[str, Dict[str, List[float]]]:
+    out: Dict[str, Dict[str, List[float]]] = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in sorted(glob.glob(path_glob)):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                out[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def _avg(v: List[float]) -> float:
+    return sum(v) / len(v) if v else 0.0
+
+
+def cmd_stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    lines = [f"# {args.title}", "", "Command:", "", "```", args.cmd, "```", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("vc::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+        name = name.replace("void ", "").split("(")[0]
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_traffic(args):
+    fetch = _counters(os.path.join(args.fetch, "*counter_collection.csv"))
+    write = _counters(os.path.join(args.write, "*counter_collection.csv"))
+    cf = _counters(os.path.join(args.copy_fetch, "*counter_collection.csv"))
+    cw = _counters(os.path.join(args.copy_write, "*counter_collection.csv"))
+
+    def copy_kib(c, counter):
+        vals = [v for name, d in c.items() if "copyBuffer" in name or "elementwise" in name
+                for v in d.get(counter, []) if v > 1024]
+        return max(vals) if vals else 0.0
+
+    true_kib = args.copy_bytes / 1024.0
+    f_fetch = true_kib / copy_kib(cf, "FETCH_SIZE")
+    f_write = true_kib / copy_kib(cw, "WRITE_SIZE")
+    rec = {"source_hash": attn_source_hash(), "fetch_scale": round(f_fetch, 4),
+           "write_scale": round(f_write, 4), "copy_bytes": args.copy_bytes, "command": args.cmd,
+           "kernels": {}}
+    lines = [f"# {args.title}", "", "Commands (one counter per run, then the same for the copy probe):", "",
+             "```", args.cmd, "```", "",
+             f"Copy calibration ({args.copy_bytes / 2**30:.0f} GiB device copy): FETCH_SIZE reads "
+             f"{copy_kib(cf, 'FETCH_SIZE'):.0f} KiB, WRITE_SIZE {copy_kib(cw, 'WRITE_SIZE'):.0f} KiB for "
+             f"{true_kib:.0f} KiB moved each way; scale factors {f_fetch:.3f} (fetch), {f_write:.3f} (write).",
+             "", "| kernel | launches | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | HBM bytes/launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for name in sorted(set(fetch) | set(write)):
+        role = _role(name)
+        if role is None:
+            continue
+        fk, wk = _avg(fetch[name].get("FETCH_SIZE", [])), _avg(write[name].get("WRITE_SIZE", []))
+        b = fk * 1024 * f_fetch + wk * 1024 * f_write
+        rec["kernels"][role] = {"bytes_per_launch": int(b), "fetch_kib": fk, "write_kib": wk,
+                                "launches": len(fetch[name].get("FETCH_SIZE", []))}
+        lines.append(f"| {role} | {len(fetch[name].get('FETCH_SIZE', []))} | {fk:.0f} | {wk:.0f} | {b:.4g} |")
+    if args.note:
+        lines += ["", args.note]
+    json.dump(rec, open(args.json, "w"), indent=1)
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_sq(args):
+    c = _counters(os.path.join(args.dir, "*", "*counter_collection.csv"))
+    lines = [f"# {args.title}", "", "Commands:", "", "```", args.cmd, "```", "",
+             "| kernel | counter | avg per launch |", "|---|---|---|"]
+    for name, d in sorted(c.items()):
+        role = _role(name)
+        if role is None:
+            continue
+        for counter, vals in sorted(d.items()):
+            lines.append(f"| {role} | {counter} | {_avg(vals):.4g} |")
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--title", default="Kernel trace summary")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--note", default="")
+    s.set_defaults(fn=cmd_stats)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--json", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--title", default="HBM traffic per launch")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--note", default="")
+    t.set_defaults(fn=cmd_traffic)
+    q = sub.add_parser("sq")
+    q.add_argument("--dir", required=True)
+    q.add_argument("--out", required=True)
+    q.add_argument("--title", default="SQ counters")
+    q.add_argument("--cmd", required=True)
+    q.add_argument("--note", default="")
+    q.set_defaults(fn=cmd_sq)
+    args = ap.parse_args()
+    args.fn(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,8 +23,8 @@ def tight_tol(n_keys: int, kivi: bool = False) -> float:
     return float(min(TOL_CONTRACT, 12 * base + 1e-4))
 
 
-ERRLOG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
-                      "parity_errors.txt")
+# optional log of every comparison's error (path from the environment; off by default)
+ERRLOG = os.environ.get("VC_PARITY_LOG")
 
 
 def require_gpu():
@@ -88,7 +88,7 @@ def pool_kivi(pool, layer: int, r: int, g: int, T: int, d: int):
 
 def assert_close(got: np.ndarray, want: np.ndarray, tol: float, what: str):
     err = float(np.abs(got - want).max()) if got.size else 0.0
-    if os.path.isdir(os.path.dirname(ERRLOG)):
+    if ERRLOG:
         with open(ERRLOG, "a") as f:
             f.write(f"{what}\tmax_abs={err:.3e}\ttol={tol:.1e}\n")
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
