@@ -109,3 +109,16 @@ def tokens_match(tok_gpu, tok_or, gap_or, z_or, tie=1e-3):
             continue
         bad.append((i, int(tok_gpu[i]), int(tok_or[i]), float(gap_or[i])))
     return bad
+
+
+def ctx_bits_gpu_generator(cfg, r: int, l: int, g: int, n: int, stream: int, p0: int = 0) -> np.ndarray:
+    """Context rows [p0, p0 + n) of (request r, layer l, kv head g) as uint16 [n][d], drawn by the
+    seeded generator's GPU fill kernel (vcsynth), not by the attention library.  Bit-identical to
+    vcsynth.tensors.kctx_bits / vctx_bits (pinned by a test), and much faster at full lengths."""
+    from vcsynth import gpu as sg
+    from vcsynth import tensors as T
+    t = torch.empty((n, cfg.d), dtype=torch.int16, device="cuda")
+    sg.fill_normal_bf16(t, [cfg.d, 1], T.ctx_index(cfg, r, l, g, p0, 0), cfg.seed, stream)
+    out = t.cpu().numpy().view(np.uint16).copy()
+    del t
+    return out
