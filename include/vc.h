@@ -72,9 +72,11 @@ typedef struct {
  *         halves of a word hold the even and the odd codes, so one shift and mask yields a pair)
  *   v     uint32 [L][nb][Hkv][d][16*bits/32]          codes of each channel's 16 tokens, same
  *         packing with the token index in place of the channel
- *   k_sz  fp16 [L][nb][Hkv][d][2]   (scale, zero) of each channel for the 32-token group made of
- *         logical pages 2j and 2j+1, stored in the block of page 2j (odd pages' entries unused)
- *   v_sz  fp16 [L][nb][Hkv][d/32][16][2]   (scale, zero) per channel group and token
+ *   k_sz  fp16 [L][nb][Hkv][2][d]   scale plane then zero plane: the (scale, zero) of each channel
+ *         for the 32-token group made of logical pages 2j and 2j+1, stored in the block of page 2j
+ *         (odd pages' entries unused)
+ *   v_sz  fp16 [L][nb][Hkv][d/32][2][16]   per 32-channel group: the scales of the page's 16
+ *         tokens, then their zeros
  */
 typedef struct {
   int32_t bits;                /* 16, 2 or 4 */

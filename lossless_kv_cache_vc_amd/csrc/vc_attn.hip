@@ -888,6 +888,144 @@ __device__ __forceinline__ void unpack8(const uint32_t* words, int u0, float* ou
   }
 }
 
+// One page pair (32 keys) of a draft item from global memory, dequantising KIVI codes (or
+// converting drafted-block bf16 rows) to fp16 in registers: the path for pairs the LDS ring
+// does not cover (an odd last context page, drafted-block pages).  Updates the running softmax
+// state (m_run, l_run, acc_o) of lane (row n, group kg).
+template <int D, int BITS>
+__device__ __forceinline__ void draft_pair_generic(const AttnArgs& a, const ItemCtx& it, int pp,
+                                                   const u32x4* qreg, int qpos, float sc,
+                                                   f32x4* acc_o, float& m_run, float& l_run) {
+  constexpr bool KIVI = BITS != 16;
+  constexpr int NS = D / 32;
+  constexpr int ND = D / 16;
+  const int lane = threadIdx.x & 63, n = lane & 15, kg = lane >> 4;
+  PageRef pr[2];
+  pr[0] = page_ref<D>(a, it, 2 * pp, KIVI);
+  pr[1] = page_ref<D>(a, it, 2 * pp + 1, KIVI);
+
+  // ---- scores S^T (16 keys x 16 rows) for the two 16-key blocks of the pair
+  f32x4 s_acc[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    s_acc[b] = f32x4{};
+    const int m = n;  // A-operand row = key slot m: page m/8, token 8*((m>>2)&1) + 4b + (m&3)
+    const PageRef p = (m >> 3) ? pr[1] : pr[0];
+    const int ktok = 8 * ((m >> 2) & 1) + 4 * b + (m & 3);
+    u32x4 av[NS];
+    if (p.kind == 2 || ktok >= p.valid) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) av[s] = u32x4{0, 0, 0, 0};
+    } else if (!KIVI || p.kind == 1) {
+      const uint8_t* krow = p.k + ktok * (D * 2);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        av[s] = ld16(krow + 2 * (KIVI ? draft_chan<D>(kg, s) : 32 * s + 8 * kg));
+        if constexpr (KIVI) av[s] = bf16x8_to_f16x8(av[s]);
+      }
+    } else {
+      // KIVI key row: codes of channels [kg*D/4, (kg+1)*D/4), dequantised with the
+      // per-channel (scale, zero) of this 32-token group
+      constexpr int WPG = D / 4 * BITS / 32;  // words per lane group
+      uint32_t words[WPG];
+      const uint32_t* wrow = reinterpret_cast<const uint32_t*>(p.k + ktok * (D * BITS / 8)) + kg * WPG;
+#pragma unroll
+      for (int i = 0; i < WPG; ++i) words[i] = wrow[i];
+      // planar (scale, zero) of the group: scales of channels 0..d-1, then zeros
+      const uint16_t* ksc = reinterpret_cast<const uint16_t*>(p.ksz) + kg * (D / 4);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float code[8];
+        unpack8<BITS>(words, 8 * s, code);
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const int c = 8 * s + j;
+          const float k0 = fmaf(code[j], fp16_bits_to_f32(ksc[c]), fp16_bits_to_f32(ksc[D + c]));
+          const float k1 = fmaf(code[j + 1], fp16_bits_to_f32(ksc[c + 1]), fp16_bits_to_f32(ksc[D + c + 1]));
+          pk[j >> 1] = pack_f16(k0, k1);
+        }
+        av[s] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) s_acc[b] = mfma16<KIVI>(av[s], qreg[s], s_acc[b]);
+  }
+
+  // ---- softmax over this lane's 8 keys: page kg/2, tokens 8*(kg&1) + 4b + r
+  const PageRef mp = (kg >> 1) ? pr[1] : pr[0];
+  float sv[8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 8 * (kg & 1) + 4 * b + r;
+      sv[4 * b + r] = key_visible(mp, tt, qpos) ? s_acc[b][r] : -INFINITY;
+    }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mloc = fmaxf(mloc, sv[j]);
+  mloc = wave_xor_max(mloc, 16);
+  mloc = wave_xor_max(mloc, 32);
+  const float m_new = fmaxf(m_run, mloc * sc);
+  if (__any(m_new > m_run + kLazyRescale)) {
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc_o[i][r] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  uint32_t pb[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[j], sc, -m_use));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], sc, -m_use));
+    l_run += p0 + p1;
+    pb[j >> 1] = KIVI ? pack_f16(p0, p1) : pack_bf16(p0, p1);
+  }
+  const u32x4 bv = {pb[0], pb[1], pb[2], pb[3]};
+
+  // ---- O^T += V^T P^T: lane (d = 16*db + n, kg) feeds tokens 8*(kg&1)..+8 of page kg/2
+  const PageRef& vp = mp;
+  const int t0 = 8 * (kg & 1);
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    const int dd = 16 * db + n;
+    u32x4 av = {0, 0, 0, 0};
+    if (vp.kind != 2) {
+      if (!KIVI || vp.kind == 1) {
+        av = ld16(vp.v + dd * 32 + t0 * 2);
+        if (vp.valid < kBlock) av = mask_tokens(av, t0, vp.valid);
+        if constexpr (KIVI) av = bf16x8_to_f16x8(av);
+      } else {
+        constexpr int WPC = 16 * BITS / 32;  // words per channel (16 tokens)
+        uint32_t words[WPC];
+        const uint32_t* wrow = reinterpret_cast<const uint32_t*>(vp.v) + dd * WPC;
+#pragma unroll
+        for (int i = 0; i < WPC; ++i) words[i] = wrow[i];
+        float code[8];
+        unpack8<BITS>(words, t0, code);
+        // this channel group's token scales, then token zeros
+        const uint16_t* vsc = reinterpret_cast<const uint16_t*>(vp.vsz) + (dd >> 5) * 2 * kBlock + t0;
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          float v0 = fmaf(code[j], fp16_bits_to_f32(vsc[j]), fp16_bits_to_f32(vsc[kBlock + j]));
+          float v1 = fmaf(code[j + 1], fp16_bits_to_f32(vsc[j + 1]), fp16_bits_to_f32(vsc[kBlock + j + 1]));
+          if (t0 + j >= vp.valid) v0 = 0.f;
+          if (t0 + j + 1 >= vp.valid) v1 = 0.f;
+          pk[j >> 1] = pack_f16(v0, v1);
+        }
+        av = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      }
+    }
+    acc_o[db] = mfma16<KIVI>(av, bv, acc_o[db]);
+  }
+}
+
 template <int D, int BITS, int NW>
 __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   constexpr bool KIVI = BITS != 16;
@@ -919,134 +1057,311 @@ __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) 
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
   const int npairs = (it.npages + 1) >> 1;
+  for (int pp = w; pp < npairs; pp += NW)
+    draft_pair_generic<D, BITS>(a, it, pp, qreg, qpos, sc, acc_o, m_run, l_run);
 
-  for (int pp = w; pp < npairs; pp += NW) {
-    PageRef pr[2];
-    pr[0] = page_ref<D>(a, it, 2 * pp, KIVI);
-    pr[1] = page_ref<D>(a, it, 2 * pp + 1, KIVI);
+  // ---- merge the waves' states through LDS
+  l_run = wave_xor_sum(l_run, 16);
+  l_run = wave_xor_sum(l_run, 32);
+  draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
+}
 
-    // ---- scores S^T (16 keys x 16 rows) for the two 16-key blocks of the pair
+// ------------------------------------------------------------------ draft path, KIVI caches (ring)
+// Whole context page pairs (one 32-token key-quantisation group each) stream through a private
+// per-wave LDS ring, as in the bf16 draft path.  The scales are folded out of the inner loops:
+//   scores   q.k^ = sum_c code_c (s_c q_c) + sum_c z_c q_c       (key scale/zero per channel)
+//   outputs  sum_t p_t v^_t,c = sum_t code_t,c (s_t,g p_t) + sum_t z_t,g p_t   (value per token)
+// so the per-element work is only turning 2- or 4-bit codes into exact fp16 values: the two codes
+// of a pair-interleaved word field land in the mantissas of 1024.0h (0x6400) and one packed
+// subtraction of 1024 leaves (c0, c1).  Products run on 16x16x32 fp16 MFMA.  The per-row key
+// bias is added to the scores of each pair; the value bias is accumulated per channel group and
+// added to the outputs once the ring pairs are done.  Pairs the ring does not cover (an odd last
+// context page, drafted-block pages) go through draft_pair_generic.
+template <int D, int BITS, int NW>
+struct KRing {
+  static constexpr int kCodes = kBlock * D * BITS / 8;    // one page's key (or value) codes
+  static constexpr int kKsz = 2 * D * 2;                  // key scale and zero planes of a group
+  static constexpr int kVsz = (D / 32) * 2 * kBlock * 2;  // value scales and zeros of a page
+  static constexpr int kOffV = 2 * kCodes;
+  static constexpr int kOffKsz = 4 * kCodes;
+  static constexpr int kOffVsz = kOffKsz + kKsz;
+  static constexpr int kSlot = (kOffVsz + 2 * kVsz + 1023) / 1024 * 1024;
+  static constexpr int kLoads = 7;                          // ring loads per slot
+  static constexpr int kIds = 144 * 1024 * D / 128;         // LDS offset of the page ids
+  static constexpr int kStg0 = kIds / (NW * kSlot);
+  static constexpr int kStg = kStg0 > 8 ? 8 : kStg0;        // slots per wave
+  static constexpr int kBytes = kIds + kMaxChunkPages * 4;
+};
+
+// wait until at most `ahead` slots (PER loads each) of this wave are still in flight
+template <int PER, int A>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmem<0>();
+  } else {
+    if (ahead >= A) wait_vmem<A * PER>();
+    else wait_ahead<PER, A - 1>(ahead);
+  }
+}
+
+// ring load of one contiguous piece of `bytes` (a multiple of 16, at most 1024) into LDS `dst`
+template <int BYTES>
+__device__ __forceinline__ void ring_piece(const uint8_t* src, uint8_t* dst, int lane) {
+  static_assert(BYTES % 16 == 0 && BYTES <= 1024, "ring piece");
+  if (BYTES == 1024 || lane < BYTES / 16) {
+    const void* s = src + 16 * lane;
+    __builtin_amdgcn_global_load_lds(s, (lds_ptr_t)dst, 16, 0, kNontemporal);
+  }
+}
+
+// exact fp16 values of code pair j (codes 2j and 2j+1) of a pair-interleaved word
+template <int BITS>
+__device__ __forceinline__ uint32_t code_pair_f16(uint32_t w, int j) {
+  constexpr uint32_t M = ((1u << BITS) - 1u) * 0x00010001u;
+  const uint32_t biased = ((w >> (BITS * j)) & M) | 0x64006400u;  // 1024 + c in each half
+  const f16x2 v = __builtin_bit_cast(f16x2, biased) - f16x2{(_Float16)1024.f, (_Float16)1024.f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Vector elements are copied to scalars before __builtin_bit_cast: a cast applied to a
+// subscripted ext_vector lvalue reads the vector's first element whatever the index.
+__device__ __forceinline__ u32x4 mul_f16x8(u32x4 a, u32x4 b) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ai = a[i], bi = b[i];
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ai) * __builtin_bit_cast(f16x2, bi));
+  }
+  return r;
+}
+
+__device__ __forceinline__ float dot_f16x8(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ai = a[i], bi = b[i];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, ai), __builtin_bit_cast(f16x2, bi), acc, false);
+  }
+  return acc;
+}
+
+// sum over the 4 lanes of a row (lanes n, n + 16, n + 32, n + 48)
+__device__ __forceinline__ float row_sum4(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return half_swap_sum(__builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float row_max4(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return half_swap_max(fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])));
+}
+
+template <int D, int BITS, int NW>
+__device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
+  using R = KRing<D, BITS, NW>;
+  constexpr int STG = R::kStg;
+  static_assert(STG >= 2, "KIVI draft ring needs two slots per wave");
+  constexpr int NS = D / 32;              // k-steps of the score product
+  constexpr int ND = D / 16;              // 16-wide channel blocks of the output
+  constexpr int NGQ = D / 32;             // value channel groups
+  constexpr int PER = 32 / BITS;          // codes per word
+  constexpr int KW = (D / 4) * BITS / 32; // words of a key row held by one lane (its D/4 channels)
+  constexpr int VW = kBlock * BITS / 32;  // words of a value channel row (16 tokens)
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const ReqDev& rq = it.rq;
+  const int G = a.G;
+  const bool row_ok = n < it.rows_total;
+  const int tok = row_ok ? n / G : 0;
+  const int qpos = rq.q0 + tok;
+
+  // query of row n, channels kg * D/4 .. + D/4 (8 per k-step), in fp16
+  u32x4 qh[NS];
+  {
+    const uint16_t* qp = a.q + ((((int64_t)rq.slot * a.L + it.l) * a.xmax + rq.q0 + tok) * a.Hq +
+                                it.g * G + (row_ok ? n % G : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qh[s] = bf16x8_to_f16x8(row_ok ? ld16(qp + draft_chan<D>(kg, s)) : u32x4{0, 0, 0, 0});
+  }
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + R::kIds);
+  {
+    const PoolDev& pl = it.pool;
+    const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
+    for (int i = tid; i < it.nctx; i += 64 * NW) {
+      const int phys = pt[i];
+      ids[i] = (phys < 0 || phys >= pl.nblk) ? -1 : phys;
+    }
+  }
+  wait_vmem<0>();
+  __syncthreads();
+
+  const PoolDev& pl = it.pool;
+  const int64_t unit0 = (int64_t)it.l * pl.nblk * a.Hkv + it.g;  // block 0 of (layer, kv head)
+  uint8_t* ring = smem + w * (STG * R::kSlot);
+  const int ring_pairs = it.nctx >> 1;  // pairs of two context pages
+  const int mine = ring_pairs > w ? (ring_pairs - w + NW - 1) / NW : 0;
+  auto issue = [&](int k, int id0, int id1) {
+    uint8_t* slot = ring + (k % STG) * R::kSlot;
+    const int64_t u0 = unit0 + (int64_t)(id0 < 0 ? 0 : id0) * a.Hkv;
+    const int64_t u1 = unit0 + (int64_t)(id1 < 0 ? 0 : id1) * a.Hkv;
+    ring_piece<R::kCodes>(pl.k + u0 * R::kCodes, slot, lane);
+    ring_piece<R::kCodes>(pl.k + u1 * R::kCodes, slot + R::kCodes, lane);
+    ring_piece<R::kCodes>(pl.v + u0 * R::kCodes, slot + R::kOffV, lane);
+    ring_piece<R::kCodes>(pl.v + u1 * R::kCodes, slot + R::kOffV + R::kCodes, lane);
+    ring_piece<R::kKsz>(pl.ksz + u0 * R::kKsz, slot + R::kOffKsz, lane);
+    ring_piece<R::kVsz>(pl.vsz + u0 * R::kVsz, slot + R::kOffVsz, lane);
+    ring_piece<R::kVsz>(pl.vsz + u1 * R::kVsz, slot + R::kOffVsz + R::kVsz, lane);
+  };
+  auto pair_ids = [&](int k, int& id0, int& id1) {
+    const int pp = w + NW * k;
+    id0 = k < mine ? ids[2 * pp] : 0;
+    id1 = k < mine ? ids[2 * pp + 1] : 0;
+  };
+#pragma unroll
+  for (int k = 0; k < STG - 1; ++k)
+    if (k < mine) {
+      int i0, i1;
+      pair_ids(k, i0, i1);
+      issue(k, __builtin_amdgcn_readfirstlane(i0), __builtin_amdgcn_readfirstlane(i1));
+    }
+  int pf0, pf1;  // page ids of the next slot to load, read one pair early
+  pair_ids(STG - 1, pf0, pf1);
+
+  f32x4 acc_o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc_o[i] = f32x4{};
+  float vb[NGQ];  // value-zero bias per channel group (this lane's tokens)
+#pragma unroll
+  for (int i = 0; i < NGQ; ++i) vb[i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+  const int vtok0 = 8 * (kg & 1), vpage = kg >> 1;  // this lane's 8 tokens of a pair
+
+  for (int k = 0; k < mine; ++k) {
+    wait_ahead<R::kLoads, STG - 2>(min(STG - 2, mine - 1 - k));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (k + STG - 1 < mine) issue(k + STG - 1, __builtin_amdgcn_readfirstlane(pf0), __builtin_amdgcn_readfirstlane(pf1));
+    pair_ids(k + STG, pf0, pf1);
+
+    const uint8_t* slot = ring + (k % STG) * R::kSlot;
+    const int pp = w + NW * k;
+    // ---- page validity (full pairs need no masking)
+    const int ip0 = 2 * pp;
+    const int v0 = ids[ip0] < 0 ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0));
+    // the odd page's keys use the group parameters stored with the even page
+    const int v1 = (ids[ip0] < 0 || ids[ip0 + 1] < 0) ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0 + 1));
+    const bool full = v0 == kBlock && v1 == kBlock;
+
+    // ---- key side: q' = q * scale (per channel), bias = sum_c zero_c q_c of row n
+    u32x4 qs[NS];
+    float kb = 0.f;
+    {
+      const uint16_t* ksc = reinterpret_cast<const uint16_t*>(slot + R::kOffKsz) + kg * (D / 4);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qs[s] = mul_f16x8(qh[s], ld16(ksc + 8 * s));
+        kb = dot_f16x8(qh[s], ld16(ksc + D + 8 * s), kb);
+      }
+    }
+    kb = row_sum4(kb);
+    // ---- scores S^T for the pair's two 16-key halves: A-operand row m is key (page m / 8,
+    // token 8 ((m >> 2) & 1) + 4 b + (m & 3)), so lane (n, kg) ends with tokens 8 (kg & 1) + 4 b + i
+    // of page kg / 2 -- exactly the B operand of the value product
     f32x4 s_acc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
+      const int tk = 8 * ((n >> 2) & 1) + 4 * b + (n & 3);
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(slot + (n >> 3) * R::kCodes + tk * (D * BITS / 8)) + kg * KW;
+      uint32_t words[KW];
+#pragma unroll
+      for (int i = 0; i < KW; ++i) words[i] = kw[i];
       s_acc[b] = f32x4{};
-      const int m = n;  // A-operand row = key slot m: page m/8, token 8*((m>>2)&1) + 4b + (m&3)
-      const PageRef p = (m >> 3) ? pr[1] : pr[0];
-      const int ktok = 8 * ((m >> 2) & 1) + 4 * b + (m & 3);
-      u32x4 av[NS];
-      if (p.kind == 2 || ktok >= p.valid) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) av[s] = u32x4{0, 0, 0, 0};
-      } else if (!KIVI || p.kind == 1) {
-        const uint8_t* krow = p.k + ktok * (D * 2);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          av[s] = ld16(krow + 2 * (KIVI ? draft_chan<D>(kg, s) : 32 * s + 8 * kg));
-          if constexpr (KIVI) av[s] = bf16x8_to_f16x8(av[s]);
-        }
-      } else {
-        // KIVI key row: codes of channels [kg*D/4, (kg+1)*D/4), dequantised with the
-        // per-channel (scale, zero) of this 32-token group
-        constexpr int WPG = D / 4 * BITS / 32;  // words per lane group
-        uint32_t words[WPG];
-        const uint32_t* wrow = reinterpret_cast<const uint32_t*>(p.k + ktok * (D * BITS / 8)) + kg * WPG;
-#pragma unroll
-        for (int i = 0; i < WPG; ++i) words[i] = wrow[i];
-        const uint32_t* szp = reinterpret_cast<const uint32_t*>(p.ksz) + kg * (D / 4);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          float code[8];
-          unpack8<BITS>(words, 8 * s, code);
-          uint32_t pk[4];
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            const uint32_t sz0 = szp[8 * s + j], sz1 = szp[8 * s + j + 1];
-            const float k0 = fmaf(code[j], fp16_bits_to_f32(sz0 & 0xFFFF), fp16_bits_to_f32(sz0 >> 16));
-            const float k1 = fmaf(code[j + 1], fp16_bits_to_f32(sz1 & 0xFFFF), fp16_bits_to_f32(sz1 >> 16));
-            pk[j >> 1] = pack_f16(k0, k1);
-          }
-          av[s] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        }
+      for (int s = 0; s < NS; ++s) {
+        const int u0 = 8 * s;  // first of this k-step's 8 codes among the lane's channels
+        const uint32_t wv = words[u0 / PER];
+        const int j0 = (u0 % PER) / 2;
+        const u32x4 av = {code_pair_f16<BITS>(wv, j0), code_pair_f16<BITS>(wv, j0 + 1),
+                          code_pair_f16<BITS>(wv, j0 + 2), code_pair_f16<BITS>(wv, j0 + 3)};
+        s_acc[b] = mfma16<true>(av, qs[s], s_acc[b]);
       }
-#pragma unroll
-      for (int s = 0; s < NS; ++s) s_acc[b] = mfma16<KIVI>(av[s], qreg[s], s_acc[b]);
     }
-
-    // ---- softmax over this lane's 8 keys: page kg/2, tokens 8*(kg&1) + 4b + r
-    const PageRef mp = (kg >> 1) ? pr[1] : pr[0];
+    // ---- online softmax over this lane's 8 keys
     float sv[8];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = 8 * (kg & 1) + 4 * b + r;
-        sv[4 * b + r] = key_visible(mp, tt, qpos) ? s_acc[b][r] : -INFINITY;
-      }
-    float mloc = -INFINITY;
+      for (int i = 0; i < 4; ++i) sv[4 * b + i] = s_acc[b][i] + kb;
+    if (!full) {
+      const int valid = vpage ? v1 : v0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mloc = fmaxf(mloc, sv[j]);
-    mloc = wave_xor_max(mloc, 16);
-    mloc = wave_xor_max(mloc, 32);
+      for (int j = 0; j < 8; ++j)
+        if (vtok0 + j >= valid) sv[j] = -INFINITY;
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mloc = row_max4(mloc);
     const float m_new = fmaxf(m_run, mloc * sc);
     if (__any(m_new > m_run + kLazyRescale)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < ND; ++i)
+      for (int i = 0; i < ND; ++i) acc_o[i] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc_o[i][r] *= alpha;
+      for (int i = 0; i < NGQ; ++i) vb[i] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    uint32_t pb[4];
+    uint32_t ph[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[j], sc, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], sc, -m_use));
-      l_run += p0 + p1;
-      pb[j >> 1] = KIVI ? pack_f16(p0, p1) : pack_bf16(p0, p1);
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[j], sc, -m_use));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], sc, -m_use));
+      l_run += e0 + e1;
+      ph[j >> 1] = pack_f16(e0, e1);
     }
-    const u32x4 bv = {pb[0], pb[1], pb[2], pb[3]};
-
-    // ---- O^T += V^T P^T: lane (d = 16*db + n, kg) feeds tokens 8*(kg&1)..+8 of page kg/2
-    const PageRef& vp = mp;
-    const int t0 = 8 * (kg & 1);
+    const u32x4 p16 = {ph[0], ph[1], ph[2], ph[3]};
+    // ---- value side: P'_g = p * scale_t,g and bias_g += sum_t zero_t,g p_t, per channel group
+    const uint16_t* vsz = reinterpret_cast<const uint16_t*>(slot + R::kOffVsz + vpage * R::kVsz) + vtok0;
+    const uint8_t* vcodes = slot + R::kOffV + vpage * R::kCodes;
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int dd = 16 * db + n;
-      u32x4 av = {0, 0, 0, 0};
-      if (vp.kind != 2) {
-        if (!KIVI || vp.kind == 1) {
-          av = ld16(vp.v + dd * 32 + t0 * 2);
-          if (vp.valid < kBlock) av = mask_tokens(av, t0, vp.valid);
-          if constexpr (KIVI) av = bf16x8_to_f16x8(av);
-        } else {
-          constexpr int WPC = 16 * BITS / 32;  // words per channel (16 tokens)
-          uint32_t words[WPC];
-          const uint32_t* wrow = reinterpret_cast<const uint32_t*>(vp.v) + dd * WPC;
-#pragma unroll
-          for (int i = 0; i < WPC; ++i) words[i] = wrow[i];
-          float code[8];
-          unpack8<BITS>(words, t0, code);
-          const uint32_t* szp = reinterpret_cast<const uint32_t*>(vp.vsz) + (dd >> 5) * kBlock + t0;
-          uint32_t pk[4];
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            const uint32_t sz0 = szp[j], sz1 = szp[j + 1];
-            float v0 = fmaf(code[j], fp16_bits_to_f32(sz0 & 0xFFFF), fp16_bits_to_f32(sz0 >> 16));
-            float v1 = fmaf(code[j + 1], fp16_bits_to_f32(sz1 & 0xFFFF), fp16_bits_to_f32(sz1 >> 16));
-            if (t0 + j >= vp.valid) v0 = 0.f;
-            if (t0 + j + 1 >= vp.valid) v1 = 0.f;
-            pk[j >> 1] = pack_f16(v0, v1);
-          }
-          av = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        }
+    for (int gq = 0; gq < NGQ; ++gq) {
+      u32x4 vs = ld16(vsz + (2 * gq) * kBlock);
+      u32x4 vz = ld16(vsz + (2 * gq + 1) * kBlock);
+      if (!full) {  // tokens past the page's valid ones may hold any bits: no scale, no zero
+        const int valid = vpage ? v1 : v0;
+        vs = mask_tokens(vs, vtok0, valid);
+        vz = mask_tokens(vz, vtok0, valid);
       }
-      acc_o[db] = mfma16<KIVI>(av, bv, acc_o[db]);
+      const u32x4 pv = mul_f16x8(p16, vs);
+      vb[gq] = dot_f16x8(p16, vz, vb[gq]);
+      // O^T += V^T P'^T for the two 16-channel blocks of this group
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int db = 2 * gq + h2;
+        const int dd = 16 * db + n;
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vcodes + dd * (kBlock * BITS / 8));
+        const uint32_t wv = vw[vtok0 / PER];
+        const int j0 = (vtok0 % PER) / 2;
+        const u32x4 av = {code_pair_f16<BITS>(wv, j0), code_pair_f16<BITS>(wv, j0 + 1),
+                          code_pair_f16<BITS>(wv, j0 + 2), code_pair_f16<BITS>(wv, j0 + 3)};
+        acc_o[db] = mfma16<true>(av, pv, acc_o[db]);
+      }
     }
   }
 
-  // ---- merge the waves' states through LDS
+  // the value bias joins the outputs before any pair that rescales without it
+#pragma unroll
+  for (int gq = 0; gq < NGQ; ++gq) {
+    const float t = row_sum4(vb[gq]);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) acc_o[2 * gq + h2] += t;
+  }
+  // pairs outside the ring: an odd last context page and the drafted block
+  const int npairs = (it.npages + 1) >> 1;
+  for (int pp = ring_pairs + w; pp < npairs; pp += NW)
+    draft_pair_generic<D, BITS>(a, it, pp, qh, qpos, sc, acc_o, m_run, l_run);
+
+  __syncthreads();  // every wave is done with its ring before the merge reuses the LDS
   l_run = wave_xor_sum(l_run, 16);
   l_run = wave_xor_sum(l_run, 32);
   draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
@@ -1092,8 +1407,8 @@ template <int D, int NW>
 __device__ __forceinline__ void draft_dispatch(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   const int bits = it.pool.bits;
   if (bits == 16) draft_bf16_item<D, NW, (NW <= 4 ? 4 : 2)>(a, it, smem);
-  else if (bits == 2) draft_item<D, 2, NW>(a, it, smem);
-  else draft_item<D, 4, NW>(a, it, smem);
+  else if (bits == 2) draft_kivi_item<D, 2, NW>(a, it, smem);
+  else draft_kivi_item<D, 4, NW>(a, it, smem);
 }
 
 // Verify items only: 8 waves, one work-group per CU (the ring takes most of the LDS).
@@ -1117,18 +1432,21 @@ __global__ __launch_bounds__(kDThreads) void draft_bf16_kernel(const AttnArgs a)
 }
 
 template <int D, int BITS>
-__global__ __launch_bounds__(kDThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void draft_kivi_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DraftSmem<D>::kBytes];
+__global__ __launch_bounds__(kDThreads) void draft_kivi_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[KRing<D, BITS, kDWaves>::kBytes];
   ItemCtx it;
   int rg;
   if (!decode_item(a, &it, &rg)) return;
-  draft_item<D, BITS, kDWaves>(a, it, smem);
+  draft_kivi_item<D, BITS, kDWaves>(a, it, smem);
 }
 
 // One launch over a mixed list (drafting and verifying requests of a batch together).
 template <int D>
 __global__ __launch_bounds__(kVThreads) void mixed_kernel(const AttnArgs a) {
-  constexpr int kBytes = VRing<D>::kBytes > DRing<D>::kBytes ? VRing<D>::kBytes : DRing<D>::kBytes;
+  constexpr int kA = VRing<D>::kBytes > DRing<D>::kBytes ? VRing<D>::kBytes : DRing<D>::kBytes;
+  constexpr int kB = KRing<D, 2, kVWaves>::kBytes > KRing<D, 4, kVWaves>::kBytes ? KRing<D, 2, kVWaves>::kBytes
+                                                                                  : KRing<D, 4, kVWaves>::kBytes;
+  constexpr int kBytes = kA > kB ? kA : kB;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes];
   ItemCtx it;
   int rg;

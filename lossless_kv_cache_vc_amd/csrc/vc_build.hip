@@ -340,8 +340,8 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
     for (int t = 0; t < 32; ++t)
       ck[t][c] = t < cnt ? (uint8_t)quant_code(bf16_to_f64(xk[t][c]), s16, z16, levels) : 0;
     uint16_t* ksz = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.ksz) + unit_e * (D * 4));
-    ksz[2 * c] = s16;
-    ksz[2 * c + 1] = z16;
+    ksz[c] = s16;       // scale plane
+    ksz[D + c] = z16;   // zero plane
   }
   // values: one (token, 32-channel group) per thread
   for (int task = threadIdx.x; task < 32 * (D / 32); task += blockDim.x) {
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
       const int phys = dst.page_table[(int64_t)r * dst.max_pages + page];
       const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
       uint16_t* vsz = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.vsz) + unit * (D / 32 * kBlock * 4));
-      vsz[(gq * kBlock + tt) * 2] = s16;
-      vsz[(gq * kBlock + tt) * 2 + 1] = z16;
+      vsz[(gq * 2) * kBlock + tt] = s16;      // [group][scale plane][token]
+      vsz[(gq * 2 + 1) * kBlock + tt] = z16;  // [group][zero plane][token]
     } else {
       for (int c = 32 * gq; c < 32 * gq + 32; ++c) cv[t][c] = 0;
     }

@@ -90,8 +90,8 @@ class Workload:
         d, L, Hkv = cfg.d, cfg.L, cfg.Hkv
         k = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
         v = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
-        ksz = torch.empty((L, nblk, Hkv, d, 2), dtype=torch.int16, device=self.dev)
-        vsz = torch.empty((L, nblk, Hkv, d // 32, 16, 2), dtype=torch.int16, device=self.dev)
+        ksz = torch.empty((L, nblk, Hkv, 2, d), dtype=torch.int16, device=self.dev)
+        vsz = torch.empty((L, nblk, Hkv, d // 32, 2, 16), dtype=torch.int16, device=self.dev)
         return vc.PagedPool(bits, torch.from_numpy(pt).to(self.dev), k, v, nblk, ksz, vsz)
 
     @staticmethod

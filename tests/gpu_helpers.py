@@ -74,13 +74,13 @@ def pool_kivi(pool, layer: int, r: int, g: int, T: int, d: int):
         kc.append(unpack_codes(kw, bits, d))                            # [16][d]
         vw = pool.v[layer, b, g].cpu().numpy().view(np.uint32).reshape(d, 16 * bits // 32)
         vc_.append(unpack_codes(vw, bits, 16).T)                        # [16][d]
-        vsz = pool.v_sz[layer, b, g].cpu().numpy().view(np.float16)     # [d/32][16][2]
-        vs.append(vsz[:, :, 0].T)
-        vz.append(vsz[:, :, 1].T)
+        vsz = pool.v_sz[layer, b, g].cpu().numpy().view(np.float16)     # [d/32][2][16]
+        vs.append(vsz[:, 0, :].T)
+        vz.append(vsz[:, 1, :].T)
         if p % 2 == 0:
-            ksz = pool.k_sz[layer, b, g].cpu().numpy().view(np.float16)  # [d][2]
-            ks.append(ksz[:, 0])
-            kz.append(ksz[:, 1])
+            ksz = pool.k_sz[layer, b, g].cpu().numpy().view(np.float16)  # [2][d]
+            ks.append(ksz[0])
+            kz.append(ksz[1])
     return dict(kcodes=np.concatenate(kc)[:T], vcodes=np.concatenate(vc_)[:T],
                 kscale=np.stack(ks), kzero=np.stack(kz),
                 vscale=np.concatenate(vs)[:T], vzero=np.concatenate(vz)[:T])
