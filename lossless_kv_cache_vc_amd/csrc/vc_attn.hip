@@ -28,8 +28,10 @@ namespace vc {
 
 namespace {
 
-constexpr int kDWaves = 4;            // waves of a draft-only work-group
+constexpr int kDWaves = 4;            // waves of a draft-only work-group (bf16 caches)
 constexpr int kDThreads = 64 * kDWaves;
+constexpr int kKWaves = 8;            // waves of a draft-only work-group (KIVI caches): two per SIMD
+constexpr int kKThreads = 64 * kKWaves;
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -1071,12 +1073,14 @@ __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) 
 // per-wave LDS ring, as in the bf16 draft path.  The scales are folded out of the inner loops:
 //   scores   q.k^ = sum_c code_c (s_c q_c) + sum_c z_c q_c       (key scale/zero per channel)
 //   outputs  sum_t p_t v^_t,c = sum_t code_t,c (s_t,g p_t) + sum_t z_t,g p_t   (value per token)
-// so the per-element work is only turning 2- or 4-bit codes into exact fp16 values: the two codes
-// of a pair-interleaved word field land in the mantissas of 1024.0h (0x6400) and one packed
-// subtraction of 1024 leaves (c0, c1).  Products run on 16x16x32 fp16 MFMA.  The per-row key
-// bias is added to the scores of each pair; the value bias is accumulated per channel group and
-// added to the outputs once the ring pairs are done.  Pairs the ring does not cover (an odd last
-// context page, drafted-block pages) go through draft_pair_generic.
+// so the per-element work is only expanding 2- or 4-bit codes to exact fp16 (one and-or per
+// pair, see pair_at).  Every product runs on 16x16x32 fp16 MFMA, the bias terms included: with
+// an A operand that is the same for every row (the zeros of the lane's channels or tokens, or the
+// negated expansion offsets), one MFMA sums over all 32 keys of the k-step, so the bias of row n
+// lands in every output row of column n without cross-lane sums.  Key biases initialise the score
+// accumulators; value biases accumulate per 32-channel group and join the outputs once the ring
+// pairs are done.  Pairs the ring does not cover (an odd last context page, drafted-block pages)
+// go through draft_pair_generic.
 template <int D, int BITS, int NW>
 struct KRing {
   static constexpr int kCodes = kBlock * D * BITS / 8;    // one page's key (or value) codes
@@ -1114,13 +1118,46 @@ __device__ __forceinline__ void ring_piece(const uint8_t* src, uint8_t* dst, int
   }
 }
 
-// exact fp16 values of code pair j (codes 2j and 2j+1) of a pair-interleaved word
+// Code expansion.  A pair of codes sitting at mantissa bits [p, p + BITS) of both 16-bit
+// halves of a word becomes two exact fp16 values with one and-or: the or-ed exponent makes
+// mantissa bit p worth 1, so each half reads 2^(10 - p) + code.  The constant 2^(10 - p) is the
+// pair's offset; the MFMAs that consume the expanded codes cancel it with one more product of
+// the negated offsets (row-independent A operand) against the same B operand.
+//   2-bit: a word holds 8 pairs (pair i at bits 2i of each half).  Pairs 0-3 are rotated left
+//          by 2 and pairs 4-7 right by 6, which puts them at bits 2, 4, 6, 8: offsets 256, 64,
+//          16, 4.
+//   4-bit: a word holds 4 pairs (pair i at bits 4i).  A left rotation by 2 puts pairs 0 and 1
+//          at bits 2 and 6, a right rotation by 6 does the same for pairs 2 and 3: offsets 256,
+//          16, 256, 16.
+// Bits rotated across a half boundary land outside every mask.
+// One v_and_or_b32 per pair: the mask comes from an SGPR and the exponent from a VGPR, since a
+// VOP3 instruction of this architecture takes no literal operand (the compiler would otherwise
+// split it into an and and an or with literals).
+__device__ __forceinline__ uint32_t pair_at(uint32_t x, int p, int bits) {
+  const uint32_t mask = (((1u << bits) - 1u) << p) * 0x00010001u;
+  const uint32_t magic = ((uint32_t)(25 - p) << 10) * 0x00010001u;
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+  return r;
+}
+
+// the 4 pairs (8 codes) of 2-bit word `w` selected by `hi` (0: pairs 0-3, 1: pairs 4-7)
+__device__ __forceinline__ u32x4 expand_2bit(uint32_t w, int hi) {
+  const uint32_t x = __builtin_rotateright32(w, hi ? 6 : 30);
+  return u32x4{pair_at(x, 2, 2), pair_at(x, 4, 2), pair_at(x, 6, 2), pair_at(x, 8, 2)};
+}
+
+// the 4 pairs (8 codes) of 4-bit word `w`
+__device__ __forceinline__ u32x4 expand_4bit(uint32_t w) {
+  const uint32_t x0 = __builtin_rotateright32(w, 30), x1 = __builtin_rotateright32(w, 6);
+  return u32x4{pair_at(x0, 2, 4), pair_at(x0, 6, 4), pair_at(x1, 2, 4), pair_at(x1, 6, 4)};
+}
+
+// negated offsets of the expanded pairs, as an fp16 A operand (the same for every row)
 template <int BITS>
-__device__ __forceinline__ uint32_t code_pair_f16(uint32_t w, int j) {
-  constexpr uint32_t M = ((1u << BITS) - 1u) * 0x00010001u;
-  const uint32_t biased = ((w >> (BITS * j)) & M) | 0x64006400u;  // 1024 + c in each half
-  const f16x2 v = __builtin_bit_cast(f16x2, biased) - f16x2{(_Float16)1024.f, (_Float16)1024.f};
-  return __builtin_bit_cast(uint32_t, v);
+__device__ __forceinline__ u32x4 neg_offsets() {
+  if constexpr (BITS == 2) return u32x4{0xDC00DC00u, 0xD400D400u, 0xCC00CC00u, 0xC400C400u};  // -256 -64 -16 -4
+  else return u32x4{0xDC00DC00u, 0xCC00CC00u, 0xDC00DC00u, 0xCC00CC00u};                   // -256 -16 -256 -16
 }
 
 // Vector elements are copied to scalars before __builtin_bit_cast: a cast applied to a
@@ -1135,21 +1172,7 @@ __device__ __forceinline__ u32x4 mul_f16x8(u32x4 a, u32x4 b) {
   return r;
 }
 
-__device__ __forceinline__ float dot_f16x8(u32x4 a, u32x4 b, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t ai = a[i], bi = b[i];
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, ai), __builtin_bit_cast(f16x2, bi), acc, false);
-  }
-  return acc;
-}
-
-// sum over the 4 lanes of a row (lanes n, n + 16, n + 32, n + 48)
-__device__ __forceinline__ float row_sum4(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return half_swap_sum(__builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]));
-}
+// maximum over the 4 lanes of a row (lanes n, n + 16, n + 32, n + 48)
 __device__ __forceinline__ float row_max4(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -1164,9 +1187,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   constexpr int NS = D / 32;              // k-steps of the score product
   constexpr int ND = D / 16;              // 16-wide channel blocks of the output
   constexpr int NGQ = D / 32;             // value channel groups
-  constexpr int PER = 32 / BITS;          // codes per word
   constexpr int KW = (D / 4) * BITS / 32; // words of a key row held by one lane (its D/4 channels)
-  constexpr int VW = kBlock * BITS / 32;  // words of a value channel row (16 tokens)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
   const ReqDev& rq = it.rq;
   const int G = a.G;
@@ -1230,9 +1251,10 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   f32x4 acc_o[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc_o[i] = f32x4{};
-  float vb[NGQ];  // value-zero bias per channel group (this lane's tokens)
+  f32x4 vb[NGQ];  // value bias of each channel group: sum_t p_t (z_t - offsets s_t), per column
 #pragma unroll
-  for (int i = 0; i < NGQ; ++i) vb[i] = 0.f;
+  for (int i = 0; i < NGQ; ++i) vb[i] = f32x4{};
+  const u32x4 noff = neg_offsets<BITS>();
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
   const int vtok0 = 8 * (kg & 1), vpage = kg >> 1;  // this lane's 8 tokens of a pair
@@ -1252,18 +1274,18 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     const int v1 = (ids[ip0] < 0 || ids[ip0 + 1] < 0) ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0 + 1));
     const bool full = v0 == kBlock && v1 == kBlock;
 
-    // ---- key side: q' = q * scale (per channel), bias = sum_c zero_c q_c of row n
+    // ---- key side: q' = q * scale (per channel); bias of column n = sum_c (z_c q_c - off_c q'_c)
     u32x4 qs[NS];
-    float kb = 0.f;
+    f32x4 kb = f32x4{};
     {
       const uint16_t* ksc = reinterpret_cast<const uint16_t*>(slot + R::kOffKsz) + kg * (D / 4);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         qs[s] = mul_f16x8(qh[s], ld16(ksc + 8 * s));
-        kb = dot_f16x8(qh[s], ld16(ksc + D + 8 * s), kb);
+        kb = mfma16<true>(ld16(ksc + D + 8 * s), qh[s], kb);
+        kb = mfma16<true>(noff, qs[s], kb);
       }
     }
-    kb = row_sum4(kb);
     // ---- scores S^T for the pair's two 16-key halves: A-operand row m is key (page m / 8,
     // token 8 ((m >> 2) & 1) + 4 b + (m & 3)), so lane (n, kg) ends with tokens 8 (kg & 1) + 4 b + i
     // of page kg / 2 -- exactly the B operand of the value product
@@ -1275,14 +1297,11 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       uint32_t words[KW];
 #pragma unroll
       for (int i = 0; i < KW; ++i) words[i] = kw[i];
-      s_acc[b] = f32x4{};
+      s_acc[b] = kb;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int u0 = 8 * s;  // first of this k-step's 8 codes among the lane's channels
-        const uint32_t wv = words[u0 / PER];
-        const int j0 = (u0 % PER) / 2;
-        const u32x4 av = {code_pair_f16<BITS>(wv, j0), code_pair_f16<BITS>(wv, j0 + 1),
-                          code_pair_f16<BITS>(wv, j0 + 2), code_pair_f16<BITS>(wv, j0 + 3)};
+        // the lane's channels 8s .. 8s + 7
+        const u32x4 av = BITS == 2 ? expand_2bit(words[s >> 1], s & 1) : expand_4bit(words[s]);
         s_acc[b] = mfma16<true>(av, qs[s], s_acc[b]);
       }
     }
@@ -1291,7 +1310,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * b + i] = s_acc[b][i] + kb;
+      for (int i = 0; i < 4; ++i) sv[4 * b + i] = s_acc[b][i];
     if (!full) {
       const int valid = vpage ? v1 : v0;
 #pragma unroll
@@ -1320,7 +1339,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       ph[j >> 1] = pack_f16(e0, e1);
     }
     const u32x4 p16 = {ph[0], ph[1], ph[2], ph[3]};
-    // ---- value side: P'_g = p * scale_t,g and bias_g += sum_t zero_t,g p_t, per channel group
+    // ---- value side: P'_g = p * scale_t,g; bias_g += sum_t (z_t,g p_t - off_t P'_t,g)
     const uint16_t* vsz = reinterpret_cast<const uint16_t*>(slot + R::kOffVsz + vpage * R::kVsz) + vtok0;
     const uint8_t* vcodes = slot + R::kOffV + vpage * R::kCodes;
 #pragma unroll
@@ -1333,17 +1352,16 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
         vz = mask_tokens(vz, vtok0, valid);
       }
       const u32x4 pv = mul_f16x8(p16, vs);
-      vb[gq] = dot_f16x8(p16, vz, vb[gq]);
+      vb[gq] = mfma16<true>(vz, p16, vb[gq]);
+      vb[gq] = mfma16<true>(noff, pv, vb[gq]);
       // O^T += V^T P'^T for the two 16-channel blocks of this group
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int db = 2 * gq + h2;
         const int dd = 16 * db + n;
         const uint32_t* vw = reinterpret_cast<const uint32_t*>(vcodes + dd * (kBlock * BITS / 8));
-        const uint32_t wv = vw[vtok0 / PER];
-        const int j0 = (vtok0 % PER) / 2;
-        const u32x4 av = {code_pair_f16<BITS>(wv, j0), code_pair_f16<BITS>(wv, j0 + 1),
-                          code_pair_f16<BITS>(wv, j0 + 2), code_pair_f16<BITS>(wv, j0 + 3)};
+        // the lane's tokens vtok0 .. vtok0 + 7 of channel dd
+        const u32x4 av = BITS == 2 ? expand_2bit(vw[0], kg & 1) : expand_4bit(vw[kg & 1]);
         acc_o[db] = mfma16<true>(av, pv, acc_o[db]);
       }
     }
@@ -1352,9 +1370,8 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   // the value bias joins the outputs before any pair that rescales without it
 #pragma unroll
   for (int gq = 0; gq < NGQ; ++gq) {
-    const float t = row_sum4(vb[gq]);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) acc_o[2 * gq + h2] += t;
+    acc_o[2 * gq] += vb[gq];
+    acc_o[2 * gq + 1] += vb[gq];
   }
   // pairs outside the ring: an odd last context page and the drafted block
   const int npairs = (it.npages + 1) >> 1;
@@ -1432,12 +1449,12 @@ __global__ __launch_bounds__(kDThreads) void draft_bf16_kernel(const AttnArgs a)
 }
 
 template <int D, int BITS>
-__global__ __launch_bounds__(kDThreads) void draft_kivi_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[KRing<D, BITS, kDWaves>::kBytes];
+__global__ __launch_bounds__(kKThreads) void draft_kivi_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[KRing<D, BITS, kKWaves>::kBytes];
   ItemCtx it;
   int rg;
   if (!decode_item(a, &it, &rg)) return;
-  draft_kivi_item<D, BITS, kDWaves>(a, it, smem);
+  draft_kivi_item<D, BITS, kKWaves>(a, it, smem);
 }
 
 // One launch over a mixed list (drafting and verifying requests of a batch together).
@@ -1507,14 +1524,14 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
     if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
     else if (has_v) hipLaunchKernelGGL(verify_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
     else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<128>, grid, dim3(kDThreads), 0, stream, args);
-    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<128, 2>), grid, dim3(kDThreads), 0, stream, args);
-    else hipLaunchKernelGGL((draft_kivi_kernel<128, 4>), grid, dim3(kDThreads), 0, stream, args);
+    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<128, 2>), grid, dim3(kKThreads), 0, stream, args);
+    else hipLaunchKernelGGL((draft_kivi_kernel<128, 4>), grid, dim3(kKThreads), 0, stream, args);
   } else {
     if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
     else if (has_v) hipLaunchKernelGGL(verify_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
     else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<64>, grid, dim3(kDThreads), 0, stream, args);
-    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<64, 2>), grid, dim3(kDThreads), 0, stream, args);
-    else hipLaunchKernelGGL((draft_kivi_kernel<64, 4>), grid, dim3(kDThreads), 0, stream, args);
+    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<64, 2>), grid, dim3(kKThreads), 0, stream, args);
+    else hipLaunchKernelGGL((draft_kivi_kernel<64, 4>), grid, dim3(kKThreads), 0, stream, args);
   }
   int rc = hip_check(hipGetLastError(), "attention launch");
   if (rc) return rc;
