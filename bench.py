@@ -27,10 +27,10 @@ METRIC = "verify+draft attention achieved HBM TB/s (% of peak), Llama-3.1-8B sha
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def measured_traffic(kind: str):
-    """HBM bytes per launch of one attention kernel from the committed rocprofv3 counter runs
-    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when absent or
-    taken on other kernel code."""
+def measured_traffic(config: str, kind: str):
+    """HBM bytes per launch of one attention kernel of one workload from the committed rocprofv3
+    counter runs (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when
+    absent or taken on other kernel code."""
     from lossless_kv_cache_vc_amd.profiling import attn_source_hash
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -38,7 +38,7 @@ def measured_traffic(kind: str):
         return None
     if rec.get("source_hash") != attn_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kind)
+    k = rec.get("configs", {}).get(config, {}).get("kernels", {}).get(kind)
     return None if not k else k.get("bytes_per_launch")
 
 
@@ -111,7 +111,7 @@ def bench_mixed(cfg, wl, args):
            "data": "synthetic", "config": {"workload": f"{cfg.name}: {cfg.note}", "requests": cfg.B,
                                           "parallelism": "1 GPU"},
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("mixed"),
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.config, "mixed"),
                         "kernel": "mixed_kernel<128>", "algorithmic_bytes_per_launch": int(nbytes)},
            "breakdown_ms": {"launch": round(ms, 4)}}
     print(json.dumps(out), flush=True)
@@ -195,7 +195,7 @@ def main():
         else:
             achieved, per_launch, name, role = draft_gbps, sum(d_bytes) / x, draft_name, draft_role
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(role),
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.config, role),
                 "kernel": name, "algorithmic_bytes_per_launch": int(per_launch)}
 
     # verify MFMA use: the two bf16 products (scores and weighted values) of every query row

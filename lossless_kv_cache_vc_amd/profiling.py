@@ -3,11 +3,12 @@
 Measurement tooling only (it reads CSV files; it launches nothing on the GPU).
 
 * ``stats``   — per-kernel average duration from ``--kernel-trace --stats -f csv`` output.
-* ``traffic`` — HBM bytes per launch of the attention kernels from two ``--pmc`` runs
-  (``FETCH_SIZE``, then ``WRITE_SIZE``, KiB per dispatch), each scaled by what the same counter
-  reads for a plain device copy of known size (``copy_probe.py``).  The result is written as
-  JSON together with a hash of the attention source, so a later change to the kernels makes the
-  stored traffic stale (the benchmark then reports ``null``).
+* ``traffic`` — HBM bytes per launch of the attention kernels of one workload from two ``--pmc``
+  runs (``FETCH_SIZE``, then ``WRITE_SIZE``, KiB per dispatch), each scaled by what the same
+  counter reads for a plain device copy of known size (``copy_probe.py``).  The result is merged
+  into a JSON file (one entry per workload) together with a hash of the attention source, so a
+  later change to the kernels makes the stored traffic stale (the benchmark then reports
+  ``null``).
 * ``sq``      — instruction and MFMA counters of the verify kernel (utilisation figures).
 
     python -m lossless_kv_cache_vc_amd.profiling stats --csv DIR/x_kernel_stats.csv --out profiles/a.md --cmd "..."
@@ -92,9 +93,17 @@ def cmd_traffic(args):
     true_kib = args.copy_bytes / 1024.0
     f_fetch = true_kib / copy_kib(cf, "FETCH_SIZE")
     f_write = true_kib / copy_kib(cw, "WRITE_SIZE")
-    rec = {"source_hash": attn_source_hash(), "fetch_scale": round(f_fetch, 4),
-           "write_scale": round(f_write, 4), "copy_bytes": args.copy_bytes, "command": args.cmd,
-           "kernels": {}}
+    try:
+        rec = json.load(open(args.json))
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_hash") != attn_source_hash():
+        rec = {}
+    rec.update({"source_hash": attn_source_hash(), "fetch_scale": round(f_fetch, 4),
+                "write_scale": round(f_write, 4), "copy_bytes": args.copy_bytes})
+    rec.setdefault("configs", {})
+    entry = {"command": args.cmd, "kernels": {}}
+    rec["configs"][args.config] = entry
     lines = [f"# {args.title}", "", "Commands (one counter per run, then the same for the copy probe):", "",
              "```", args.cmd, "```", "",
              f"Copy calibration ({args.copy_bytes / 2**30:.0f} GiB device copy): FETCH_SIZE reads "
@@ -108,8 +117,8 @@ def cmd_traffic(args):
             continue
         fk, wk = _avg(fetch[name].get("FETCH_SIZE", [])), _avg(write[name].get("WRITE_SIZE", []))
         b = fk * 1024 * f_fetch + wk * 1024 * f_write
-        rec["kernels"][role] = {"bytes_per_launch": int(b), "fetch_kib": fk, "write_kib": wk,
-                                "launches": len(fetch[name].get("FETCH_SIZE", []))}
+        entry["kernels"][role] = {"bytes_per_launch": int(b), "fetch_kib": fk, "write_kib": wk,
+                                  "launches": len(fetch[name].get("FETCH_SIZE", []))}
         lines.append(f"| {role} | {len(fetch[name].get('FETCH_SIZE', []))} | {fk:.0f} | {wk:.0f} | {b:.4g} |")
     if args.note:
         lines += ["", args.note]
@@ -148,6 +157,7 @@ def main():
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--config", required=True, help="workload id the counters were taken on (e.g. C2)")
     t.add_argument("--json", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--title", default="HBM traffic per launch")
