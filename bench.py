@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle work to time for the CPU baseline")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="0: greedy accept; > 0: drafted tokens sampled at this temperature and the "
+                         "rejection-sampling accept")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: every (request, "
@@ -158,14 +161,16 @@ def main():
         evs[1].record()
         wl.run_verify()
         evs[2].record()
-        wl.logits_and_accept()
+        wl.logits()
         evs[3].record()
+        wl.accept(args.temperature)
+        evs[4].record()
 
     for _ in range(args.warmup):
-        one_round([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        one_round([torch.cuda.Event(enable_timing=True) for _ in range(5)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -175,7 +180,8 @@ def main():
 
     draft_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    tail_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    logits_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    accept_ms = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
     attn_ms = draft_ms + verify_ms
     value_tbs = round_bytes / (attn_ms * 1e-3) / 1e12
     ms_per_step = wall * 1e3 / args.steps
@@ -230,7 +236,9 @@ def main():
         "verify_mfma": {"achieved": round(v_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(v_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": int(v_flops)},
         "breakdown_ms": {"draft_total": round(draft_ms, 3), "draft_per_launch": round(draft_launch_ms, 4),
-                         "verify": round(verify_ms, 3), "logits_accept": round(tail_ms, 3)},
+                         "verify": round(verify_ms, 3), "logits": round(logits_ms, 3),
+                         "accept": round(accept_ms, 4)},
+        "accept": "greedy" if args.temperature <= 0 else f"rejection sampling, T = {args.temperature}",
         "bytes": {"verify": v_bytes, "draft_per_step_avg": int(sum(d_bytes) / x), "round": round_bytes},
     }
     if not args.no_cpu_baseline:

@@ -162,6 +162,44 @@ int vc_accept(int n_inst, int max_x, int max_xv, int vocab, const int32_t* x, co
               void* stream);
 
 /*
+ * Drafter-side sampling at temperature T > 0 (VeriCache review, §Implementation notes worth
+ * absorbing, "Rejection sampling for non-greedy": the drafter samples its token from its own
+ * distribution).  For each row r: p = softmax(logits[r] / T) in float64, and tokens[r] is the
+ * smallest k with p_0 + ... + p_k > u[r] * sum(p) (inverse CDF; if rounding leaves no such k, the
+ * last k with p_k > 0).
+ *   logits fp32 [rows][vocab] (finite), u fp64 [rows] uniforms in (0, 1), tokens int32 [rows];
+ *   all device pointers, caller-owned.  Asynchronous on `stream`.
+ * Errors (nothing launched): VC_EINVAL for rows < 0, vocab < 1, T not finite and > 0, NULL.
+ */
+int vc_sample_tokens(int rows, int vocab, float temperature, const float* logits, const double* u,
+                     int32_t* tokens, void* stream);
+
+/*
+ * Rejection-sampling accept at temperature T > 0 (VeriCache review, §Implementation notes worth
+ * absorbing, "Rejection sampling for non-greedy"; the greedy rule is vc_accept).  For instance i
+ * with x[i] drafted slots and xv[i] verifier rows (x[i] or x[i] + 1), slot j in order:
+ *   p_lossy = softmax(draft_logits[i][j] / T), p_full = softmax(verify_logits[i][j] / T) (float64);
+ *   the drafted token t = draft_tok[i][j] is kept when u_accept[i][j] * p_lossy(t) < p_full(t)
+ *   (probability min(1, p_full(t) / p_lossy(t)); a t outside [0, vocab) is never kept);
+ *   at the first slot not kept: accept_len[i] = j and next_tok[i] is drawn with u_resample[i][j]
+ *   from max(p_full - p_lossy, 0) (from p_full if that has no mass), by the inverse CDF of
+ *   vc_sample_tokens.
+ * If every slot is kept: accept_len[i] = x[i], and next_tok[i] is drawn from p_full of verifier row
+ * x[i] with u_resample[i][x[i]] when xv[i] = x[i] + 1, else -1.  (xv[i] < x[i] ends the block at
+ * xv[i] slots.)
+ *   x, xv int32 [n_inst]; draft_logits fp32 [n_inst][max_x][vocab]; verify_logits fp32
+ *   [n_inst][max_xv][vocab]; draft_tok int32 [n_inst][max_x]; u_accept fp64 [n_inst][max_x];
+ *   u_resample fp64 [n_inst][max_x + 1] (uniforms in (0, 1)); accept_len, next_tok int32
+ *   [n_inst].  Device pointers, caller-owned; asynchronous on `stream`.
+ * Errors (nothing launched): VC_EINVAL for n_inst < 0, max_x not in [1, 64], max_xv not in
+ * [1, 65], vocab < 1, T not finite and > 0, NULL arguments.
+ */
+int vc_accept_sampled(int n_inst, int max_x, int max_xv, int vocab, float temperature, const int32_t* x,
+                      const int32_t* xv, const float* draft_logits, const float* verify_logits,
+                      const int32_t* draft_tok, const double* u_accept, const double* u_resample,
+                      int32_t* accept_len, int32_t* next_tok, void* stream);
+
+/*
  * LM-head stand-in used to turn attention outputs into logits: z[r][v] = sum_w o[r][w] * W_u[w][v]
  * (fp32 accumulate).  o fp32 [rows][width] with row stride ld_o floats; w_u bf16 [width][vocab];
  * z fp32 [rows][vocab].  VeriCache review, §Draft–Verify Pipeline: argmax over the logits of

@@ -1,0 +1,232 @@
+// Rejection-sampling accept (temperature > 0) and the drafter's sampling step.
+//
+// VeriCache review, §Implementation notes worth absorbing, "Rejection sampling for non-greedy":
+// the drafter samples t_i from its own distribution p_lossy; the verifier keeps t_i with
+// probability min(1, p_full(t_i) / p_lossy(t_i)); at the first slot it does not keep, one token
+// is drawn from the residual (p_full - p_lossy, negative parts removed) and the block ends; the
+// emitted tokens then follow p_full exactly.
+//
+// Probabilities are float64 softmax(z / T) of the fp32 logits.  The keep test compares
+// u * p_lossy(t) with p_full(t) (no division).  A draw takes one uniform u in (0, 1) and returns
+// the smallest index whose prefix sum exceeds u times the total weight (inverse CDF).  Uniforms
+// are inputs: the caller owns the random numbers.
+//
+// One work-group per row (sampling) or per drafted block (accept).  A draw sums contiguous
+// chunks of the vocabulary per thread, scans the chunk sums, and lets the thread whose chunk
+// holds the crossing walk it.
+#include <limits.h>
+#include <math.h>
+
+#include "vc_internal.h"
+
+namespace vc {
+
+namespace {
+
+constexpr int kSThreads = 256;
+constexpr int kSWaves = kSThreads / 64;
+
+struct SampleLds {
+  double part[kSWaves];
+  int ipart[kSWaves];
+  double chunk[kSThreads];  // chunk sums, then their exclusive prefix
+  double total;
+  int flag;
+};
+
+__device__ double block_sum(double v, SampleLds& s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kSWaves; ++i) t += s.part[i];
+  return t;
+}
+
+__device__ double block_max(double v, SampleLds& s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = s.part[0];
+#pragma unroll
+  for (int i = 1; i < kSWaves; ++i) t = fmax(t, s.part[i]);
+  return t;
+}
+
+__device__ int block_min_int(int v, SampleLds& s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.ipart[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = s.ipart[0];
+#pragma unroll
+  for (int i = 1; i < kSWaves; ++i) t = min(t, s.ipart[i]);
+  return t;
+}
+
+__device__ int block_max_int(int v, SampleLds& s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.ipart[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = s.ipart[0];
+#pragma unroll
+  for (int i = 1; i < kSWaves; ++i) t = max(t, s.ipart[i]);
+  return t;
+}
+
+// softmax(z / T) of one row: p(k) = exp((z_k - m) / T) / s
+struct Softmax {
+  const float* z;
+  double m, s, t;
+  __device__ double p(int k) const { return exp(((double)z[k] - m) / t) / s; }
+};
+
+__device__ Softmax row_softmax(const float* z, int vocab, double t, SampleLds& s) {
+  double mx = -INFINITY;
+  for (int k = threadIdx.x; k < vocab; k += kSThreads) mx = fmax(mx, (double)z[k]);
+  Softmax r{z, block_max(mx, s), 1.0, t};
+  double e = 0.0;
+  for (int k = threadIdx.x; k < vocab; k += kSThreads) e += exp(((double)z[k] - r.m) / t);
+  r.s = block_sum(e, s);
+  return r;
+}
+
+// Inverse-CDF draw with uniform u from the non-negative weights w(k), k < vocab.
+template <class W>
+__device__ int block_draw(const W& w, int vocab, double u, SampleLds& s) {
+  const int per = (vocab + kSThreads - 1) / kSThreads;
+  const int k0 = min((int)threadIdx.x * per, vocab), k1 = min(k0 + per, vocab);
+  double cs = 0.0;
+  for (int k = k0; k < k1; ++k) cs += w(k);
+  __syncthreads();
+  s.chunk[threadIdx.x] = cs;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double run = 0.0;
+    for (int i = 0; i < kSThreads; ++i) {
+      const double c = s.chunk[i];
+      s.chunk[i] = run;
+      run += c;
+    }
+    s.total = run;
+  }
+  __syncthreads();
+  const double target = u * s.total;
+  double run = s.chunk[threadIdx.x];
+  int found = INT_MAX, last = -1;
+  for (int k = k0; k < k1; ++k) {
+    const double wk = w(k);
+    run += wk;
+    if (wk > 0.0) last = k;
+    if (found == INT_MAX && run > target) found = k;
+  }
+  found = block_min_int(found, s);
+  if (found == INT_MAX) found = block_max_int(last, s);  // rounding left u * total above every prefix
+  return found < 0 ? 0 : found;
+}
+
+__global__ __launch_bounds__(kSThreads) void sample_kernel(int vocab, double t, const float* logits,
+                                                           const double* u, int32_t* tokens) {
+  __shared__ SampleLds s;
+  const int row = blockIdx.x;
+  const Softmax sm = row_softmax(logits + (int64_t)row * vocab, vocab, t, s);
+  const int tok = block_draw([&](int k) { return sm.p(k); }, vocab, u[row], s);
+  if (threadIdx.x == 0) tokens[row] = tok;
+}
+
+__global__ __launch_bounds__(kSThreads) void accept_sampled_kernel(int max_x, int max_xv, int vocab, double t,
+                                                                   const int32_t* x, const int32_t* xv,
+                                                                   const float* dl, const float* vl,
+                                                                   const int32_t* dtok, const double* ua,
+                                                                   const double* ur, int32_t* alen,
+                                                                   int32_t* ntok) {
+  __shared__ SampleLds s;
+  const int inst = blockIdx.x;
+  const int nx = min(max(x[inst], 0), max_x), nxv = min(max(xv[inst], 0), max_xv);
+  const int nslots = min(nx, nxv);  // a slot needs its verifier row
+  for (int i = 0; i < nslots; ++i) {
+    const Softmax pl = row_softmax(dl + ((int64_t)inst * max_x + i) * vocab, vocab, t, s);
+    const Softmax pf = row_softmax(vl + ((int64_t)inst * max_xv + i) * vocab, vocab, t, s);
+    if (threadIdx.x == 0) {
+      const int tok = dtok[(int64_t)inst * max_x + i];
+      // a token outside the vocabulary is never kept
+      s.flag = (tok >= 0 && tok < vocab) ? (ua[(int64_t)inst * max_x + i] * pl.p(tok) < pf.p(tok)) : 0;
+    }
+    __syncthreads();
+    const bool keep = s.flag != 0;
+    __syncthreads();
+    if (keep) continue;
+    auto resid = [&](int k) { return fmax(pf.p(k) - pl.p(k), 0.0); };
+    double r = 0.0;
+    for (int k = threadIdx.x; k < vocab; k += kSThreads) r += resid(k);
+    r = block_sum(r, s);
+    const double u = ur[(int64_t)inst * (max_x + 1) + i];
+    const int tok = r > 0.0 ? block_draw(resid, vocab, u, s) : block_draw([&](int k) { return pf.p(k); }, vocab, u, s);
+    if (threadIdx.x == 0) {
+      alen[inst] = i;
+      ntok[inst] = tok;
+    }
+    return;
+  }
+  // every slot kept: the bonus token comes from the verifier's extra row, if there is one
+  int next = -1;
+  if (nxv > nslots && nslots == nx) {
+    const Softmax pf = row_softmax(vl + ((int64_t)inst * max_xv + nx) * vocab, vocab, t, s);
+    next = block_draw([&](int k) { return pf.p(k); }, vocab, ur[(int64_t)inst * (max_x + 1) + nx], s);
+  }
+  if (threadIdx.x == 0) {
+    alen[inst] = nslots;
+    ntok[inst] = next;
+  }
+}
+
+}  // namespace
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" {
+
+int vc_sample_tokens(int rows, int vocab, float temperature, const float* logits, const double* u,
+                     int32_t* tokens, void* stream) {
+  set_error("");
+  if (rows < 0) return fail(VC_EINVAL, "rows must be >= 0");
+  if (rows == 0) return VC_OK;
+  if (vocab < 1) return fail(VC_EINVAL, "vocab must be >= 1");
+  if (!(temperature > 0.f) || !isfinite(temperature)) return fail(VC_EINVAL, "temperature must be finite and > 0");
+  if (!logits || !u || !tokens) return fail(VC_EINVAL, "NULL argument");
+  hipLaunchKernelGGL(sample_kernel, dim3(rows), dim3(kSThreads), 0, static_cast<hipStream_t>(stream), vocab,
+                     (double)temperature, logits, u, tokens);
+  return hip_check(hipGetLastError(), "sample launch");
+}
+
+int vc_accept_sampled(int n_inst, int max_x, int max_xv, int vocab, float temperature, const int32_t* x,
+                      const int32_t* xv, const float* draft_logits, const float* verify_logits,
+                      const int32_t* draft_tok, const double* u_accept, const double* u_resample,
+                      int32_t* accept_len, int32_t* next_tok, void* stream) {
+  set_error("");
+  if (n_inst < 0) return fail(VC_EINVAL, "n_inst must be >= 0");
+  if (n_inst == 0) return VC_OK;
+  if (max_x < 1 || max_x > VC_MAX_ROWS) return fail(VC_EINVAL, "max_x must be in [1, 64]");
+  if (max_xv < 1 || max_xv > VC_MAX_ROWS + 1) return fail(VC_EINVAL, "max_xv must be in [1, 65]");
+  if (vocab < 1) return fail(VC_EINVAL, "vocab must be >= 1");
+  if (!(temperature > 0.f) || !isfinite(temperature)) return fail(VC_EINVAL, "temperature must be finite and > 0");
+  if (!x || !xv || !draft_logits || !verify_logits || !draft_tok || !u_accept || !u_resample || !accept_len ||
+      !next_tok)
+    return fail(VC_EINVAL, "NULL argument");
+  hipLaunchKernelGGL(accept_sampled_kernel, dim3(n_inst), dim3(kSThreads), 0, static_cast<hipStream_t>(stream),
+                     max_x, max_xv, vocab, (double)temperature, x, xv, draft_logits, verify_logits, draft_tok,
+                     u_accept, u_resample, accept_len, next_tok);
+  return hip_check(hipGetLastError(), "sampled accept launch");
+}
+
+}  // extern "C"

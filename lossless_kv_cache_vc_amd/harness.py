@@ -11,6 +11,7 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
+import numpy as np
 import torch
 
 from vcsynth import configs as C
@@ -237,7 +238,8 @@ class Workload:
             self._ws_cache = cache
         return t
 
-    def logits_and_accept(self):
+    def logits(self):
+        """LM-head stand-in for both passes (z_v, z_d: [B*L*xmax][vocab] fp32)."""
         cfg = self.cfg
         B, L, xm, V = cfg.B, cfg.L, self.xmax, cfg.vocab
         width = cfg.Hq * cfg.d
@@ -253,8 +255,29 @@ class Workload:
             self.next_tok = torch.empty(B * L, dtype=torch.int32, device=self.dev)
         vc.logits(rows, width, V, self.out_v, width, self.w_u, self.z_v)
         vc.logits(rows, width, V, self.out_d, width, self.w_u, self.z_d)
-        vc.accept(B * L, xm, xm, V, self.x_dev, self.x_dev, self.z_d, self.z_v, self.tok_d, self.tok_v,
-                  self.acc_len, self.next_tok)
+
+    def accept(self, temperature: float = 0.0):
+        """Greedy accept (temperature 0), or drafted tokens sampled from the drafter's logits and
+        the rejection-sampling accept (seeded uniforms, generated once).  Needs logits()."""
+        cfg = self.cfg
+        B, L, xm, V = cfg.B, cfg.L, self.xmax, cfg.vocab
+        if temperature <= 0:
+            vc.accept(B * L, xm, xm, V, self.x_dev, self.x_dev, self.z_d, self.z_v, self.tok_d, self.tok_v,
+                      self.acc_len, self.next_tok)
+            return
+        if not hasattr(self, "u_draft"):
+            idx = np.arange(B * L * xm, dtype=np.int64)
+            self.u_draft = torch.from_numpy(rng.uniform01(cfg.seed, rng.STREAM_UDRAFT, idx)).to(self.dev)
+            self.u_acc = torch.from_numpy(rng.uniform01(cfg.seed, rng.STREAM_UACC, idx)).to(self.dev)
+            self.u_res = torch.from_numpy(rng.uniform01(cfg.seed, rng.STREAM_URES,
+                                                        np.arange(B * L * (xm + 1), dtype=np.int64))).to(self.dev)
+        vc.sample_tokens(B * L * xm, V, temperature, self.z_d, self.u_draft, self.tok_d)
+        vc.accept_sampled(B * L, xm, xm, V, temperature, self.x_dev, self.x_dev, self.z_d, self.z_v, self.tok_d,
+                          self.u_acc, self.u_res, self.acc_len, self.next_tok)
+
+    def logits_and_accept(self, temperature: float = 0.0):
+        self.logits()
+        self.accept(temperature)
 
     def run_round(self):
         """x draft steps, the verify pass, logits of both, accept."""

@@ -23,6 +23,7 @@ MAX_ROWS = 64
 # every symbol include/vc.h declares
 EXPORTS = (
     "vc_attn_workspace_size", "vc_verify_attn", "vc_draft_attn", "vc_attn_mixed", "vc_accept",
+    "vc_sample_tokens", "vc_accept_sampled",
     "vc_logits", "vc_pack_bf16", "vc_select_kept", "vc_compress", "vc_stage_kv",
     "vc_last_error", "vc_version",
 )
@@ -76,6 +77,9 @@ def lib():
         L.vc_attn_mixed.argtypes = [P(Shape), i32, P(Req), vp, vp, vp, i32, P(Pool), vp, vp, sz, i32, vp]
         L.vc_accept.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.vc_logits.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp]
+        L.vc_sample_tokens.argtypes = [i32, i32, ctypes.c_float, vp, vp, vp, vp]
+        L.vc_accept_sampled.argtypes = [i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp]
         L.vc_pack_bf16.argtypes = [P(Shape), i32, vp, i32, vp, i64, P(Pool), i32, vp]
         L.vc_select_kept.argtypes = [P(Shape), i32, vp, vp, vp, vp, i64, vp, i64, vp]
         L.vc_compress.argtypes = [P(Shape), i32, vp, P(Pool), vp, i64, P(Pool), vp]
@@ -175,6 +179,19 @@ def accept(n_inst, max_x, max_xv, vocab, x, xv, draft_logits, verify_logits, dra
     _check(lib().vc_accept(n_inst, max_x, max_xv, vocab, _ptr(x), _ptr(xv), _ptr(draft_logits),
                            _ptr(verify_logits), _ptr(draft_tok), _ptr(verify_tok), _ptr(accept_len),
                            _ptr(next_tok), _stream(stream)))
+
+
+def sample_tokens(rows, vocab, temperature, logits, u, tokens, stream=None):
+    _check(lib().vc_sample_tokens(rows, vocab, temperature, _ptr(logits), _ptr(u), _ptr(tokens),
+                                  _stream(stream)))
+
+
+def accept_sampled(n_inst, max_x, max_xv, vocab, temperature, x, xv, draft_logits, verify_logits,
+                   draft_tok, u_accept, u_resample, accept_len, next_tok, stream=None):
+    _check(lib().vc_accept_sampled(n_inst, max_x, max_xv, vocab, temperature, _ptr(x), _ptr(xv),
+                                   _ptr(draft_logits), _ptr(verify_logits), _ptr(draft_tok),
+                                   _ptr(u_accept), _ptr(u_resample), _ptr(accept_len), _ptr(next_tok),
+                                   _stream(stream)))
 
 
 def logits(rows, width, vocab, o, ld_o, w_u, z, stream=None):

@@ -88,3 +88,24 @@ def test_workspace_size_accounts_for_splits():
     assert vc.attn_workspace_size(shp, [r], 400) == 0            # one split
     # 100 pages in chunks of 40 -> 3 splits of 8 rows * 4 heads, d + 4 floats each
     assert vc.attn_workspace_size(shp, [r], 40) == 2 * 2 * 3 * 8 * 4 * 132 * 4
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device pointers; host-only check")
+def test_sampling_entry_points_validate_on_host():
+    t = _FakeTensor(0x1000)
+    z = _FakeTensor(0)
+    _expect(vc.VC_EINVAL, lambda: vc.sample_tokens(-1, 16, 0.7, t, t, t, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.sample_tokens(4, 0, 0.7, t, t, t, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.sample_tokens(4, 16, 0.0, t, t, t, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.sample_tokens(4, 16, float("inf"), t, t, t, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.sample_tokens(4, 16, 0.7, t, z, t, 0))
+    vc.sample_tokens(0, 16, 0.7, t, t, t, 0)  # nothing to do: no launch, no error
+    acc = lambda n=2, mx=4, mxv=5, V=16, T=0.7, u=t: vc.accept_sampled(n, mx, mxv, V, T, t, t, t, t, t, t, u, t, t, 0)
+    _expect(vc.VC_EINVAL, lambda: acc(n=-1))
+    _expect(vc.VC_EINVAL, lambda: acc(mx=0))
+    _expect(vc.VC_EINVAL, lambda: acc(mx=65))
+    _expect(vc.VC_EINVAL, lambda: acc(mxv=66))
+    _expect(vc.VC_EINVAL, lambda: acc(V=0))
+    _expect(vc.VC_EINVAL, lambda: acc(T=-1.0))
+    _expect(vc.VC_EINVAL, lambda: acc(u=z))
+    acc(n=0)

@@ -33,6 +33,9 @@ STREAM_WU = 6
 STREAM_SCORE = 7
 STREAM_DRAWS = 8
 STREAM_PAGEPERM = 9
+STREAM_UDRAFT = 10     # uniforms of the drafter's sampling (temperature > 0)
+STREAM_UACC = 11       # uniforms of the keep test
+STREAM_URES = 12       # uniforms of the residual / bonus draw
 
 _S30 = np.uint64(30)
 _S27 = np.uint64(27)
