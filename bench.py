@@ -142,7 +142,8 @@ def main():
 
     cfg = C.get(args.config)
     t_build = time.perf_counter()
-    wl = Workload(cfg)
+    # growth room for committing one round's accepted rows after the timed region
+    wl = Workload(cfg, spare_tokens=0 if cfg.mixed else 64)
     torch.cuda.synchronize()
     print(f"# built {cfg.name} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
 
@@ -177,6 +178,17 @@ def main():
         one_round(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # commit of the last round: block rows 0..a (the accepted prefix and the token before it) of
+    # every request join the full and drafting caches (outside the metric; wall clock, incl. the
+    # host's page-table and allocator work)
+    acc = wl.acc_len.cpu().numpy()
+    counts = [min(int(acc[r * cfg.L]) + 1, cfg.reqs[r].x) for r in range(cfg.B)]
+    torch.cuda.synchronize()
+    t_c = time.perf_counter()
+    wl.commit(counts)
+    torch.cuda.synchronize()
+    commit_ms = (time.perf_counter() - t_c) * 1e3
 
     draft_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -237,7 +249,8 @@ def main():
                         "frac": round(v_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": int(v_flops)},
         "breakdown_ms": {"draft_total": round(draft_ms, 3), "draft_per_launch": round(draft_launch_ms, 4),
                          "verify": round(verify_ms, 3), "logits": round(logits_ms, 3),
-                         "accept": round(accept_ms, 4)},
+                         "accept": round(accept_ms, 4), "commit_wall": round(commit_ms, 3)},
+        "committed_rows": counts,
         "accept": "greedy" if args.temperature <= 0 else f"rejection sampling, T = {args.temperature}",
         "bytes": {"verify": v_bytes, "draft_per_step_avg": int(sum(d_bytes) / x), "round": round_bytes},
     }

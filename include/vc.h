@@ -39,13 +39,18 @@ typedef enum {
   VC_EINVAL = -1,       /* bad argument; nothing was enqueued */
   VC_ENOSPACE = -2,     /* workspace too small; nothing was enqueued */
   VC_EHIP = -3,         /* a HIP runtime call failed */
-  VC_EUNSUPPORTED = -4  /* valid but not implemented (e.g. head_dim 96) */
+  VC_EUNSUPPORTED = -4, /* valid but not implemented (e.g. head_dim 96) */
+  VC_ENOMEM = -5        /* the page allocator has too few free pages of the asked kind */
 } vc_status;
 
 #define VC_BLOCK_TOKENS 16   /* tokens per KV page */
 #define VC_MAX_REQS 64       /* requests per attention launch */
 #define VC_MAX_ROWS 64       /* drafted rows per request */
 #define VC_KIVI_GROUP 32     /* KIVI quantisation group (tokens for keys, channels for values) */
+
+/* Page kinds of the allocator (VeriCache review, §Implementation notes, "Page table tricks"). */
+#define VC_PAGE_RESIDENT 0   /* compressed-resident: allocated for the request's whole life */
+#define VC_PAGE_TRANSIENT 1  /* full-transient: allocated when the full cache is reloaded */
 
 /* Kind of work of one request in an attention launch. */
 #define VC_VERIFY 0  /* x query rows, full context + causal drafted block (MFMA row tiles) */
@@ -243,6 +248,75 @@ int vc_select_kept(const vc_shape* shape, int batch, const int32_t* lens, const 
 int vc_compress(const vc_shape* shape, int batch, const int32_t* comp_lens /* host */,
                 const vc_pool* src, const int32_t* kept, int64_t kept_stride,
                 const vc_pool* dst, void* stream);
+
+/* ---- Committing accepted rows (VeriCache review, §Draft–Verify Pipeline, the per-request cycle:
+ *      accepted drafted positions join the caches, rejected ones are rolled back) ---- */
+
+/*
+ * One request's commit: block rows 0 .. count-1 of request slot `slot` (the K/V of the inputs at
+ * positions pos .. pos+count-1: the last accepted token and the accepted drafted tokens) are
+ * appended at token positions pos .. of page-table row `page_row`.  Rows from `count` on are the
+ * rejected ones; they are simply not committed (the rollback), and the block tensor is reused.
+ * kept_len: for a token-drop cache, the number of kept positions before the commit (the new
+ * positions pos .. pos+count-1 are appended to the kept list at kept_len ..); otherwise ignored.
+ */
+typedef struct {
+  int32_t slot;
+  int32_t pos;
+  int32_t count;     /* 0 .. max_rows */
+  int32_t page_row;
+  int32_t kept_len;
+} vc_commit;
+
+/*
+ * Append the committed block rows to a bf16 pool (the full cache): for every commit, layer and kv
+ * head, block rows [0, count) go to positions [pos, pos + count) of the pool (K token-major, V
+ * channel-major pages; the page-table row must already map those positions, see
+ * vc_page_row_extend).  If kept is not NULL (int32 [batch][L][Hkv][kept_stride], device), the
+ * positions are also appended to each (slot, layer, head) kept list at kept_len .. (token drop:
+ * newly committed tokens are always kept).  blk_k / blk_v as in the attention calls.
+ * Errors (nothing launched): VC_EINVAL for a non-bf16 pool, counts outside [0, max_rows], or
+ * kept_len + count > kept_stride.
+ */
+int vc_commit_rows(const vc_shape* shape, int num, const vc_commit* commits /* host */,
+                   const void* blk_k, const void* blk_v, const vc_pool* pool, int32_t* kept,
+                   int64_t kept_stride, void* stream);
+
+/*
+ * vc_compress restricted to the tail of each request: storage positions from from_lens[r] on are
+ * rebuilt, starting at the page (bf16 drop) or 32-token key group (KIVI) that holds from_lens[r];
+ * earlier pages and groups are left as they are.  After vc_commit_rows has appended rows to the
+ * full pool (and the kept lists), this brings the compressed pool up to comp_lens[r]: a KIVI key
+ * group that gained tokens is re-quantised from its bf16 rows, so a group is final once its 32
+ * tokens are in.  vc_compress is this call with from_lens all 0.
+ */
+int vc_compress_tail(const vc_shape* shape, int batch, const int32_t* from_lens /* host */,
+                     const int32_t* comp_lens /* host */, const vc_pool* src, const int32_t* kept,
+                     int64_t kept_stride, const vc_pool* dst, void* stream);
+
+/* ---- Page allocator (host; VeriCache review, §Implementation notes, "Page table tricks": two
+ *      page kinds per request, kept apart so that transient frees do not fragment the resident
+ *      pool).  Resident blocks are ids [0, num_resident), transient ids [num_resident,
+ *      num_blocks).  Not thread-safe: one allocator per caller thread. ---- */
+
+/* Create an allocator for a pool of num_blocks blocks (*alloc = NULL on error). */
+int vc_alloc_create(int32_t num_blocks, int32_t num_resident, void** alloc);
+void vc_alloc_destroy(void* alloc);
+/* n block ids of `kind` into ids[0..n) (host); VC_ENOMEM (nothing taken) if fewer are free. */
+int vc_alloc_pages(void* alloc, int kind, int n, int32_t* ids);
+/* Give n ids of `kind` back; VC_EINVAL (nothing changed) for an id that is not allocated, of the
+ * other kind, out of range, or listed twice. */
+int vc_alloc_release(void* alloc, int kind, int n, const int32_t* ids);
+/* Free ids of `kind`, or -1 for a bad argument. */
+int32_t vc_alloc_free_count(const void* alloc, int kind);
+/* Grow one request's host page-table row from old_len to new_len tokens: blocks of `kind` for the
+ * logical pages that new_len adds (VC_ENOMEM, nothing changed, if short). */
+int vc_page_row_extend(void* alloc, int kind, int32_t* row, int32_t max_pages, int32_t old_len,
+                       int32_t new_len);
+/* Shrink a row from old_len to new_len tokens: the pages no longer needed are released and their
+ * entries set to -1 (a rollback past a page boundary, or freeing a transient full cache). */
+int vc_page_row_truncate(void* alloc, int kind, int32_t* row, int32_t max_pages, int32_t old_len,
+                         int32_t new_len);
 
 /* ---- Staging the full KV into HBM (VeriCache review, §KV Swap Scheduling: the full cache is
  *      reloaded from host memory ahead of its verify, overlapped with drafting) ---- */

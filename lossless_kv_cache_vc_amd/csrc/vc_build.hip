@@ -183,8 +183,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectInfo si, int 
 struct CompInfo {
   int32_t n;
   int32_t lens[kMaxBatch];     // stored tokens per request (k_r)
+  int32_t from[kMaxBatch];     // first stored token to rebuild (its page / group is rebuilt whole)
   int32_t base[kMaxBatch + 1];  // prefix of jobs
 };
+
+// a source position maps to a block of the source pool (bad table entries read as zeros)
+__device__ __forceinline__ bool src_ok(const PoolDev& s, int r, int pos) {
+  if (pos < 0 || pos >= s.max_pages * kBlock) return false;
+  const int phys = s.page_table[(int64_t)r * s.max_pages + pos / kBlock];
+  return phys >= 0 && phys < s.nblk;
+}
 
 // source token `pos` of (r, l, g) in a bf16 pool: key row / value element pointers
 template <int D>
@@ -209,13 +217,15 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, in
   for (int i = 1; i < ci.n; ++i)
     if (job >= ci.base[i]) r = i;
   int local = job - ci.base[r];
-  const int npages = (ci.lens[r] + kBlock - 1) / kBlock;
-  const int p = local % npages;
+  const int pfirst = ci.from[r] / kBlock;
+  const int npages = (ci.lens[r] + kBlock - 1) / kBlock - pfirst;
+  const int p = pfirst + local % npages;
   local /= npages;
   const int g = local % Hkv, l = local / Hkv;
   const int T = ci.lens[r];
   const int32_t* kp = kept ? kept + ((int64_t)(r * L + l) * Hkv + g) * kstride : nullptr;
   const int phys = dst.page_table[(int64_t)r * dst.max_pages + p];
+  if (phys < 0 || phys >= dst.nblk) return;  // unmapped destination page
   const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
   uint8_t* dk = const_cast<uint8_t*>(dst.k) + unit * (kBlock * D * 2);
   uint16_t* dv = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.v) + unit * (kBlock * D * 2));
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, in
     u32x4 v = {0, 0, 0, 0};
     if (j < T) {
       const int pos = kp ? kp[j] : j;
-      v = ld16(src_k_row<D>(src, Hkv, r, l, g, pos) + 8 * cc);
+      if (src_ok(src, r, pos)) v = ld16(src_k_row<D>(src, Hkv, r, l, g, pos) + 8 * cc);
     }
     *reinterpret_cast<u32x4*>(dk + c * 16) = v;
   }
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, in
     uint16_t v = 0;
     if (j < T) {
       const int pos = kp ? kp[j] : j;
-      v = src_v_page<D>(src, Hkv, r, l, g, pos)[dd * kBlock + pos % kBlock];
+      if (src_ok(src, r, pos)) v = src_v_page<D>(src, Hkv, r, l, g, pos)[dd * kBlock + pos % kBlock];
     }
     dv[e] = v;
   }
@@ -304,8 +314,9 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
     if (job >= ci.base[i]) r = i;
   int local = job - ci.base[r];
   const int T = ci.lens[r];
-  const int ngrp = (T + 31) / 32;
-  const int j = local % ngrp;
+  const int jfirst = ci.from[r] / 32;
+  const int ngrp = (T + 31) / 32 - jfirst;
+  const int j = jfirst + local % ngrp;
   local /= ngrp;
   const int g = local % Hkv, l = local / Hkv;
   const int t0 = 32 * j, cnt = min(32, T - t0);
@@ -316,8 +327,10 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
     uint16_t kv = 0, vv = 0;
     if (t < cnt) {
       const int pos = kp ? kp[t0 + t] : t0 + t;
-      kv = src_k_row<D>(src, Hkv, r, l, g, pos)[c];
-      vv = src_v_page<D>(src, Hkv, r, l, g, pos)[c * kBlock + pos % kBlock];
+      if (src_ok(src, r, pos)) {
+        kv = src_k_row<D>(src, Hkv, r, l, g, pos)[c];
+        vv = src_v_page<D>(src, Hkv, r, l, g, pos)[c * kBlock + pos % kBlock];
+      }
     }
     xk[t][c] = kv;
     xv[t][c] = vv;
@@ -326,6 +339,7 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
 
   const int p_even = 2 * j;
   const int phys_e = dst.page_table[(int64_t)r * dst.max_pages + p_even];
+  if (phys_e < 0 || phys_e >= dst.nblk) return;  // unmapped destination: the group is skipped
   const int64_t unit_e = ((int64_t)l * dst.nblk + phys_e) * Hkv + g;
   // keys: one channel per thread, group over the cnt tokens
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
@@ -359,10 +373,12 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
         cv[t][c] = (uint8_t)quant_code(bf16_to_f64(xv[t][c]), s16, z16, levels);
       const int page = (t0 + t) / kBlock, tt = (t0 + t) % kBlock;
       const int phys = dst.page_table[(int64_t)r * dst.max_pages + page];
-      const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
-      uint16_t* vsz = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.vsz) + unit * (D / 32 * kBlock * 4));
-      vsz[(gq * 2) * kBlock + tt] = s16;      // [group][scale plane][token]
-      vsz[(gq * 2 + 1) * kBlock + tt] = z16;  // [group][zero plane][token]
+      if (phys >= 0 && phys < dst.nblk) {
+        const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
+        uint16_t* vsz = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.vsz) + unit * (D / 32 * kBlock * 4));
+        vsz[(gq * 2) * kBlock + tt] = s16;      // [group][scale plane][token]
+        vsz[(gq * 2 + 1) * kBlock + tt] = z16;  // [group][zero plane][token]
+      }
     } else {
       for (int c = 32 * gq; c < 32 * gq + 32; ++c) cv[t][c] = 0;
     }
@@ -374,6 +390,7 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
     const int page = p_even + hp;
     if (16 * hp >= cnt) break;
     const int phys = dst.page_table[(int64_t)r * dst.max_pages + page];
+    if (phys < 0 || phys >= dst.nblk) continue;
     const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
     uint32_t* kw = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.k) + unit * (2 * D * bits));
     uint32_t* vw = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.v) + unit * (2 * D * bits));
@@ -482,8 +499,9 @@ int vc_select_kept(const vc_shape* shape, int batch, const int32_t* lens, const 
   return hip_check(hipGetLastError(), "select launch");
 }
 
-int vc_compress(const vc_shape* shape, int batch, const int32_t* comp_lens, const vc_pool* src,
-                const int32_t* kept, int64_t kept_stride, const vc_pool* dst, void* stream) {
+int vc_compress_tail(const vc_shape* shape, int batch, const int32_t* from_lens, const int32_t* comp_lens,
+                     const vc_pool* src, const int32_t* kept, int64_t kept_stride, const vc_pool* dst,
+                     void* stream) {
   set_error("");
   int rc = shape_ok(shape);
   if (rc) return rc;
@@ -500,11 +518,15 @@ int vc_compress(const vc_shape* shape, int batch, const int32_t* comp_lens, cons
   int64_t acc = 0;
   for (int i = 0; i < batch; ++i) {
     if (comp_lens[i] < 0) return fail(VC_EINVAL, "negative length");
+    const int from = from_lens ? from_lens[i] : 0;
+    if (from < 0 || from > comp_lens[i]) return fail(VC_EINVAL, "from_lens must be in [0, comp_lens]");
     if (kept && comp_lens[i] > kept_stride) return fail(VC_EINVAL, "kept_stride too small");
     if ((comp_lens[i] + kBlock - 1) / kBlock > dst->max_pages) return fail(VC_EINVAL, "dst page table too narrow");
     ci.lens[i] = comp_lens[i];
+    ci.from[i] = from;
     ci.base[i] = (int32_t)acc;
-    const int64_t per = dst->bits == 16 ? (comp_lens[i] + kBlock - 1) / kBlock : (comp_lens[i] + 31) / 32;
+    const int64_t per = dst->bits == 16 ? (comp_lens[i] + kBlock - 1) / kBlock - from / kBlock
+                                        : (comp_lens[i] + 31) / 32 - from / 32;
     acc += per * L * Hkv;
     if (acc > (1LL << 31) - 1) return fail(VC_EINVAL, "too many jobs");
   }
@@ -525,6 +547,11 @@ int vc_compress(const vc_shape* shape, int batch, const int32_t* comp_lens, cons
     else hipLaunchKernelGGL(kivi_kernel<64>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d);
   }
   return hip_check(hipGetLastError(), "compress launch");
+}
+
+int vc_compress(const vc_shape* shape, int batch, const int32_t* comp_lens, const vc_pool* src,
+                const int32_t* kept, int64_t kept_stride, const vc_pool* dst, void* stream) {
+  return vc_compress_tail(shape, batch, nullptr, comp_lens, src, kept, kept_stride, dst, stream);
 }
 
 }  // extern "C"

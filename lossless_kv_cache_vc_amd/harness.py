@@ -41,8 +41,13 @@ class Workload:
     """All device tensors of one configuration plus the launch lists of a round."""
 
     def __init__(self, cfg: C.Config, device: str = "cuda:0", build_compressed: bool = True,
-                 keep_dense_scores: bool = False):
+                 keep_dense_scores: bool = False, spare_tokens: int = 0):
+        """spare_tokens: growth room per request in every pool (page-table width, blocks handed
+        out by the library's page allocator, kept-list width) for committing accepted rows."""
         self.cfg = cfg
+        self.spare_pages = (spare_tokens + 15) // 16 + (1 if spare_tokens else 0)
+        self.spare_tokens = spare_tokens
+        self._grow = {}
         self.dev = torch.device(device)
         B, L, Hq, Hkv, d = cfg.B, cfg.L, cfg.Hq, cfg.Hkv, cfg.d
         self.xmax = round16(max(r.x for r in cfg.reqs))
@@ -64,7 +69,8 @@ class Workload:
             sg.fill_normal_bf16(self.w_u, [cfg.vocab, 1], 0, seed, rng.STREAM_WU, sigma=cfg.wu_sigma)
 
             self.lens = [r.ctx_len for r in cfg.reqs]
-            self.full = self._bf16_pool(self.lens, salt=0)
+            self.comp_lens = [r.kept for r in cfg.reqs]
+            self.full = self._bf16_pool(self.lens, salt=0, name="full")
             self._fill_full()
 
             self.out_v = torch.zeros((B, L, xm, Hq, d), dtype=torch.float32, device=dev)
@@ -77,17 +83,29 @@ class Workload:
             self.workspace = self._workspace()
 
     # ---------------------------------------------------------------- pools
-    def _bf16_pool(self, lens: List[int], salt: int) -> vc.PagedPool:
+    def _tables(self, lens: List[int], salt: int, name: str):
+        """Page tables and block count of a pool, with the growth room of spare_tokens: spare
+        blocks after the initial ones, owned by a library page allocator (resident kind)."""
         cfg = self.cfg
-        pt, nblk = C.page_tables(cfg.seed, lens, salt=salt)
+        if not self.spare_pages:
+            return C.page_tables(cfg.seed, lens, salt=salt)
+        npages = max((n + 15) // 16 for n in lens)
+        pt, nblk = C.page_tables(cfg.seed, lens, salt=salt, max_pages=npages + self.spare_pages)
+        spare = len(lens) * self.spare_pages
+        self._grow[name] = (pt, vc.PageAllocator(spare, spare), nblk)
+        return pt, nblk + spare
+
+    def _bf16_pool(self, lens: List[int], salt: int, name: str = "") -> vc.PagedPool:
+        cfg = self.cfg
+        pt, nblk = self._tables(lens, salt, name)
         shape = (cfg.L, nblk, cfg.Hkv, 16, cfg.d)
         k = torch.empty(shape, dtype=BF16, device=self.dev)
         v = torch.empty(shape, dtype=BF16, device=self.dev)
         return vc.PagedPool(16, torch.from_numpy(pt).to(self.dev), k, v, nblk)
 
-    def _kivi_pool(self, lens: List[int], bits: int, salt: int) -> vc.PagedPool:
+    def _kivi_pool(self, lens: List[int], bits: int, salt: int, name: str = "") -> vc.PagedPool:
         cfg = self.cfg
-        pt, nblk = C.page_tables(cfg.seed, lens, salt=salt)
+        pt, nblk = self._tables(lens, salt, name)
         d, L, Hkv = cfg.d, cfg.L, cfg.Hkv
         k = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
         v = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
@@ -116,7 +134,7 @@ class Workload:
             del src
 
     def comp_len(self, r: int) -> int:
-        return self.cfg.reqs[r].kept
+        return self.comp_lens[r]
 
     def drafts(self, r: int) -> bool:
         req = self.cfg.reqs[r]
@@ -135,24 +153,24 @@ class Workload:
             scores = torch.empty((B, L, Hkv, nmax), dtype=torch.int32, device=self.dev)
             sg.fill_u32(scores, [L * Hkv * NPOS, Hkv * NPOS, NPOS, 1], 0, cfg.seed, rng.STREAM_SCORE)
             kmax = max(drop_lens)
-            self.kept = torch.empty((B, L, Hkv, kmax), dtype=torch.int32, device=self.dev)
+            self.kept = torch.empty((B, L, Hkv, kmax + self.spare_tokens), dtype=torch.int32, device=self.dev)
             sel_lens = [n if k else 0 for n, k in zip(self.lens, drop_lens)]
             vc.select_kept(self.shape, sel_lens, [r.recent for r in reqs], [r.top for r in reqs],
-                           scores, nmax, self.kept, kmax)
+                           scores, nmax, self.kept, self.kept.shape[-1])
             if keep_scores:
                 self.scores = scores
             else:
                 del scores
         bf16_drop = [k if reqs[i].comp == C.COMP_DROP else 0 for i, k in enumerate(drop_lens)]
         if any(bf16_drop):
-            self.drop_pool = self._bf16_pool(bf16_drop, salt=1)
+            self.drop_pool = self._bf16_pool(bf16_drop, salt=1, name="drop")
             vc.compress(self.shape, bf16_drop, self.full, self.kept, self.kept.shape[-1], self.drop_pool)
         if any(kivi_lens):
             bits = {C.COMP_KIVI2: 2, C.COMP_DROP_KIVI4: 4}
             kinds = {reqs[i].comp for i, k in enumerate(kivi_lens) if k}
             assert len(kinds) == 1, "one KIVI bit width per workload"
             b = bits[kinds.pop()]
-            self.kivi_pool = self._kivi_pool(kivi_lens, b, salt=2)
+            self.kivi_pool = self._kivi_pool(kivi_lens, b, salt=2, name="kivi")
             with_kept = [k if reqs[i].comp == C.COMP_DROP_KIVI4 else 0 for i, k in enumerate(kivi_lens)]
             plain = [k if reqs[i].comp == C.COMP_KIVI2 else 0 for i, k in enumerate(kivi_lens)]
             if any(with_kept):
@@ -179,9 +197,9 @@ class Workload:
         for r, req in enumerate(self.cfg.reqs):
             if req.kind == C.KIND_DRAFT:
                 pool = 1 if req.comp == C.COMP_DROP else 2
-                out.append(vc.Req(r, pool, req.kept, r, req.step, 1, vc.VC_DRAFT))
+                out.append(vc.Req(r, pool, self.comp_lens[r], r, req.step, 1, vc.VC_DRAFT))
             else:
-                out.append(vc.Req(r, 0, req.ctx_len, r, 0, req.x, vc.VC_VERIFY))
+                out.append(vc.Req(r, 0, self.lens[r], r, 0, req.x, vc.VC_VERIFY))
         return out
 
     def mixed_pools(self) -> List[vc.PagedPool]:
@@ -237,6 +255,71 @@ class Workload:
             cache[key] = t
             self._ws_cache = cache
         return t
+
+    # ---------------------------------------------------------------- commit / rollback
+    def _extend(self, name: str, pool: vc.PagedPool, r: int, old: int, new: int):
+        pt, alloc, base = self._grow[name]
+        row = np.full(pt.shape[1], -1, dtype=np.int32)
+        p_old = (old + 15) // 16
+        alloc.extend_row(vc.PAGE_RESIDENT, row, old, new)      # ids of the spare range
+        p_new = (new + 15) // 16
+        if p_new > p_old:
+            pt[r, p_old:p_new] = row[p_old:p_new] + base
+            pool.page_table[r, p_old:p_new] = torch.from_numpy(pt[r, p_old:p_new].copy()).to(self.dev)
+
+    def commit(self, counts: List[int]):
+        """Append block rows [0, counts[r]) of request r (the K/V of the last accepted token and
+        of the accepted drafted tokens) to its full cache at positions lens[r] .., and to its
+        drafting cache: kept (token drop: new tokens are always kept), gathered or re-quantised
+        from the full cache by the tail rebuild.  Rows from counts[r] on are rolled back, i.e. not
+        committed.  Needs spare_tokens room."""
+        cfg = self.cfg
+        if not self.spare_pages:
+            raise ValueError("commit needs a workload built with spare_tokens > 0")
+        commits = []
+        for r, c in enumerate(counts):
+            if c <= 0:
+                continue
+            if c > cfg.reqs[r].x:
+                raise ValueError("cannot commit more rows than were drafted")
+            n, k = self.lens[r], self.comp_lens[r]
+            self._extend("full", self.full, r, n, n + c)
+            if self.drafts(r):
+                comp = cfg.reqs[r].comp
+                name, pool = ("drop", self.drop_pool) if comp == C.COMP_DROP else ("kivi", self.kivi_pool)
+                self._extend(name, pool, r, k, k + c)
+            commits.append((r, n, c, r, k))
+        if not commits:
+            return
+        kept = self.kept
+        dropped = lambda r: self.drafts(r) and cfg.reqs[r].comp in (C.COMP_DROP, C.COMP_DROP_KIVI4)
+        with_kept = [c for c in commits if dropped(c[0])]
+        without = [c for c in commits if not dropped(c[0])]
+        if with_kept:   # token drop: the committed positions also join the kept lists
+            vc.commit_rows(self.shape, with_kept, self.blk_k, self.blk_v, self.full, kept, kept.shape[-1])
+        if without:
+            vc.commit_rows(self.shape, without, self.blk_k, self.blk_v, self.full)
+        for name, pool, comps in (("drop", self.drop_pool, (C.COMP_DROP,)),
+                                  ("kivi", self.kivi_pool, (C.COMP_KIVI2, C.COMP_DROP_KIVI4))):
+            if pool is None:
+                continue
+            for with_kept in (True, False):
+                frm, to = [], []
+                for r in range(cfg.B):
+                    req = cfg.reqs[r]
+                    uses = self.drafts(r) and req.comp in comps and \
+                        (req.comp in (C.COMP_DROP, C.COMP_DROP_KIVI4)) == with_kept
+                    c = counts[r] if uses else 0
+                    frm.append(self.comp_lens[r] if uses else 0)
+                    to.append(self.comp_lens[r] + c if uses else 0)
+                if any(t > f for f, t in zip(frm, to)):
+                    vc.compress_tail(self.shape, frm, to, self.full, kept if with_kept else None,
+                                     kept.shape[-1] if (with_kept and kept is not None) else 0, pool)
+        for r, n, c, _, k in commits:
+            self.lens[r] = n + c
+            if self.drafts(r):
+                self.comp_lens[r] = k + c
+        self.workspace = self._workspace()
 
     def logits(self):
         """LM-head stand-in for both passes (z_v, z_d: [B*L*xmax][vocab] fp32)."""

@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIBVC_PATH = os.path.join(PKG, "libvc.so")
 
-VC_OK, VC_EINVAL, VC_ENOSPACE, VC_EHIP, VC_EUNSUPPORTED = 0, -1, -2, -3, -4
+VC_OK, VC_EINVAL, VC_ENOSPACE, VC_EHIP, VC_EUNSUPPORTED, VC_ENOMEM = 0, -1, -2, -3, -4, -5
+PAGE_RESIDENT, PAGE_TRANSIENT = 0, 1
 VC_VERIFY, VC_DRAFT = 0, 1
 BLOCK = 16
 MAX_REQS = 64
@@ -25,6 +26,8 @@ EXPORTS = (
     "vc_attn_workspace_size", "vc_verify_attn", "vc_draft_attn", "vc_attn_mixed", "vc_accept",
     "vc_sample_tokens", "vc_accept_sampled",
     "vc_logits", "vc_pack_bf16", "vc_select_kept", "vc_compress", "vc_stage_kv",
+    "vc_commit_rows", "vc_compress_tail", "vc_alloc_create", "vc_alloc_destroy", "vc_alloc_pages",
+    "vc_alloc_release", "vc_alloc_free_count", "vc_page_row_extend", "vc_page_row_truncate",
     "vc_last_error", "vc_version",
 )
 
@@ -46,6 +49,11 @@ class Pool(ctypes.Structure):
                 ("num_blocks", ctypes.c_int64), ("page_table", ctypes.c_void_p),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_sz", ctypes.c_void_p), ("v_sz", ctypes.c_void_p)]
+
+
+class Commit(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_int32), ("pos", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("page_row", ctypes.c_int32), ("kept_len", ctypes.c_int32)]
 
 
 class Req(ctypes.Structure):
@@ -84,8 +92,20 @@ def lib():
         L.vc_select_kept.argtypes = [P(Shape), i32, vp, vp, vp, vp, i64, vp, i64, vp]
         L.vc_compress.argtypes = [P(Shape), i32, vp, P(Pool), vp, i64, P(Pool), vp]
         L.vc_stage_kv.argtypes = [vp, vp, sz, vp, vp]
+        L.vc_commit_rows.argtypes = [P(Shape), i32, P(Commit), vp, vp, P(Pool), vp, i64, vp]
+        L.vc_compress_tail.argtypes = [P(Shape), i32, vp, vp, P(Pool), vp, i64, P(Pool), vp]
+        L.vc_alloc_create.argtypes = [ctypes.c_int32, ctypes.c_int32, P(vp)]
+        L.vc_alloc_destroy.argtypes = [vp]
+        L.vc_alloc_destroy.restype = None
+        L.vc_alloc_pages.argtypes = [vp, i32, i32, vp]
+        L.vc_alloc_release.argtypes = [vp, i32, i32, vp]
+        L.vc_alloc_free_count.argtypes = [vp, i32]
+        L.vc_alloc_free_count.restype = ctypes.c_int32
+        L.vc_page_row_extend.argtypes = [vp, i32, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.vc_page_row_truncate.argtypes = [vp, i32, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         for name in EXPORTS:
-            if name not in ("vc_last_error", "vc_version", "vc_attn_workspace_size"):
+            if name not in ("vc_last_error", "vc_version", "vc_attn_workspace_size", "vc_alloc_destroy",
+                            "vc_alloc_free_count"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -223,3 +243,58 @@ def stage_kv(dst, src_pinned, nbytes, side_stream, event=None):
 
 def version() -> str:
     return lib().vc_version().decode()
+
+
+def commit_rows(shp, commits, blk_k, blk_v, pool: "PagedPool", kept=None, kept_stride=0, stream=None):
+    """commits: (slot, pos, count, page_row, kept_len) per request."""
+    arr = (Commit * max(1, len(commits)))(*[Commit(*c) for c in commits])
+    pd = pool.desc()
+    _check(lib().vc_commit_rows(ctypes.byref(shp), len(commits), arr, _ptr(blk_k), _ptr(blk_v),
+                                ctypes.byref(pd), _ptr(kept), kept_stride, _stream(stream)))
+
+
+def compress_tail(shp, from_lens, comp_lens, src: "PagedPool", kept, kept_stride, dst: "PagedPool",
+                  stream=None):
+    sd, dd = src.desc(), dst.desc()
+    _check(lib().vc_compress_tail(ctypes.byref(shp), len(comp_lens), _i32_array(from_lens),
+                                  _i32_array(comp_lens), ctypes.byref(sd), _ptr(kept), kept_stride,
+                                  ctypes.byref(dd), _stream(stream)))
+
+
+class PageAllocator:
+    """Host page allocator of the library (resident ids [0, num_resident), transient ids above)."""
+
+    def __init__(self, num_blocks: int, num_resident: int):
+        h = ctypes.c_void_p()
+        _check(lib().vc_alloc_create(num_blocks, num_resident, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().vc_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 -- interpreter shutdown
+            pass
+
+    def alloc(self, kind: int, n: int):
+        ids = (ctypes.c_int32 * max(1, n))()
+        _check(lib().vc_alloc_pages(self._h, kind, n, ids))
+        return list(ids[:n])
+
+    def release(self, kind: int, ids):
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+        _check(lib().vc_alloc_release(self._h, kind, len(ids), arr))
+
+    def free_count(self, kind: int) -> int:
+        return int(lib().vc_alloc_free_count(self._h, kind))
+
+    def extend_row(self, kind: int, row, old_len: int, new_len: int):
+        """row: a C-contiguous numpy int32 array (one request's page-table row), updated in place."""
+        _check(lib().vc_page_row_extend(self._h, kind, row.ctypes.data, len(row), old_len, new_len))
+
+    def truncate_row(self, kind: int, row, old_len: int, new_len: int):
+        _check(lib().vc_page_row_truncate(self._h, kind, row.ctypes.data, len(row), old_len, new_len))
