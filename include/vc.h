@@ -40,7 +40,8 @@ typedef enum {
   VC_ENOSPACE = -2,     /* workspace too small; nothing was enqueued */
   VC_EHIP = -3,         /* a HIP runtime call failed */
   VC_EUNSUPPORTED = -4, /* valid but not implemented (e.g. head_dim 96) */
-  VC_ENOMEM = -5        /* the page allocator has too few free pages of the asked kind */
+  VC_ENOMEM = -5,       /* the page allocator has too few free pages of the asked kind */
+  VC_EAGAIN = -6        /* the scheduler has no room for the request now; retry after advancing */
 } vc_status;
 
 #define VC_BLOCK_TOKENS 16   /* tokens per KV page */
@@ -317,6 +318,40 @@ int vc_page_row_extend(void* alloc, int kind, int32_t* row, int32_t max_pages, i
  * entries set to -1 (a rollback past a page boundary, or freeing a transient full cache). */
 int vc_page_row_truncate(void* alloc, int kind, int32_t* row, int32_t max_pages, int32_t old_len,
                          int32_t new_len);
+
+/* ---- Admit scheduler (host; VeriCache review, §Runtime Algorithm Deep Dive: resource model,
+ *      Admit, execution loop).  A window of W future iterations and two reserve rings: the link
+ *      time of full-cache reloads per window (at most t_iter: the link is serial) and the bytes
+ *      of full caches in HBM per window (at most hbm_budget).  A reload lasts
+ *      l = KV_full / (link_bw * t_iter) iterations and occupies S = max(1, ceil(l)) windows ending
+ *      at the request's verify; its link time is spread evenly over them and its KV_full counts in
+ *      HBM for all of them.  Not thread-safe. ---- */
+
+typedef struct {
+  int32_t window;       /* W: lookahead iterations, >= 2 */
+  int32_t draft_len;    /* x: the ideal draft length (verify slot searched outward from it) */
+  double t_iter;        /* expected seconds per iteration, > 0 */
+  double link_bw;       /* host-link bytes per second, > 0 */
+  double hbm_budget;    /* bytes of HBM for full caches in flight, >= 0 */
+} vc_sched_cfg;
+
+int vc_sched_create(const vc_sched_cfg* cfg, void** sched);
+void vc_sched_destroy(void* sched);
+/* Admit(req): try verify slots d = x, x+1, x-1, x+2, ... within [S, W-1] (relative to the current
+ * iteration) and reserve the first span [d-S+1, d] that fits both rings; *verify_iter = the
+ * absolute iteration of the verify.  VC_EAGAIN (*verify_iter = -1, nothing reserved) when no span
+ * fits now; VC_EINVAL if req already holds a reservation. */
+int vc_sched_admit(void* sched, int32_t req, double kv_full_bytes, int64_t* verify_iter);
+/* End the current iteration: reservations whose verify was this iteration end, the window slides. */
+int vc_sched_advance(void* sched);
+/* The current iteration (0 after create), or -1 for NULL. */
+int64_t vc_sched_now(const void* sched);
+/* Reserved link seconds and HBM bytes of window i (0 = the current iteration). */
+int vc_sched_ring(const void* sched, int32_t i, double* link_s, double* hbm_bytes);
+/* Requests whose reload starts at the current iteration and requests that verify at it (ascending
+ * ids, at most cap of each; VC_EINVAL if more). */
+int vc_sched_due(const void* sched, int32_t cap, int32_t* reload_ids, int32_t* n_reload,
+                 int32_t* verify_ids, int32_t* n_verify);
 
 /* ---- Staging the full KV into HBM (VeriCache review, §KV Swap Scheduling: the full cache is
  *      reloaded from host memory ahead of its verify, overlapped with drafting) ---- */

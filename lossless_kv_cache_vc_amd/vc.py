@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIBVC_PATH = os.path.join(PKG, "libvc.so")
 
-VC_OK, VC_EINVAL, VC_ENOSPACE, VC_EHIP, VC_EUNSUPPORTED, VC_ENOMEM = 0, -1, -2, -3, -4, -5
+VC_OK, VC_EINVAL, VC_ENOSPACE, VC_EHIP, VC_EUNSUPPORTED, VC_ENOMEM, VC_EAGAIN = 0, -1, -2, -3, -4, -5, -6
 PAGE_RESIDENT, PAGE_TRANSIENT = 0, 1
 VC_VERIFY, VC_DRAFT = 0, 1
 BLOCK = 16
@@ -28,6 +28,8 @@ EXPORTS = (
     "vc_logits", "vc_pack_bf16", "vc_select_kept", "vc_compress", "vc_stage_kv",
     "vc_commit_rows", "vc_compress_tail", "vc_alloc_create", "vc_alloc_destroy", "vc_alloc_pages",
     "vc_alloc_release", "vc_alloc_free_count", "vc_page_row_extend", "vc_page_row_truncate",
+    "vc_sched_create", "vc_sched_destroy", "vc_sched_admit", "vc_sched_advance", "vc_sched_now",
+    "vc_sched_ring", "vc_sched_due",
     "vc_last_error", "vc_version",
 )
 
@@ -54,6 +56,11 @@ class Pool(ctypes.Structure):
 class Commit(ctypes.Structure):
     _fields_ = [("slot", ctypes.c_int32), ("pos", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("page_row", ctypes.c_int32), ("kept_len", ctypes.c_int32)]
+
+
+class SchedCfg(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("draft_len", ctypes.c_int32), ("t_iter", ctypes.c_double),
+                ("link_bw", ctypes.c_double), ("hbm_budget", ctypes.c_double)]
 
 
 class Req(ctypes.Structure):
@@ -103,9 +110,18 @@ def lib():
         L.vc_alloc_free_count.restype = ctypes.c_int32
         L.vc_page_row_extend.argtypes = [vp, i32, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.vc_page_row_truncate.argtypes = [vp, i32, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.vc_sched_create.argtypes = [P(SchedCfg), P(vp)]
+        L.vc_sched_destroy.argtypes = [vp]
+        L.vc_sched_destroy.restype = None
+        L.vc_sched_admit.argtypes = [vp, ctypes.c_int32, ctypes.c_double, P(ctypes.c_int64)]
+        L.vc_sched_advance.argtypes = [vp]
+        L.vc_sched_now.argtypes = [vp]
+        L.vc_sched_now.restype = ctypes.c_int64
+        L.vc_sched_ring.argtypes = [vp, ctypes.c_int32, P(ctypes.c_double), P(ctypes.c_double)]
+        L.vc_sched_due.argtypes = [vp, ctypes.c_int32, vp, P(ctypes.c_int32), vp, P(ctypes.c_int32)]
         for name in EXPORTS:
             if name not in ("vc_last_error", "vc_version", "vc_attn_workspace_size", "vc_alloc_destroy",
-                            "vc_alloc_free_count"):
+                            "vc_alloc_free_count", "vc_sched_destroy", "vc_sched_now"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -298,3 +314,52 @@ class PageAllocator:
 
     def truncate_row(self, kind: int, row, old_len: int, new_len: int):
         _check(lib().vc_page_row_truncate(self._h, kind, row.ctypes.data, len(row), old_len, new_len))
+
+
+class Scheduler:
+    """The library's Admit scheduler (link and HBM rings over a lookahead window)."""
+
+    def __init__(self, window: int, draft_len: int, t_iter: float, link_bw: float, hbm_budget: float):
+        self.cfg = SchedCfg(window, draft_len, t_iter, link_bw, hbm_budget)
+        h = ctypes.c_void_p()
+        _check(lib().vc_sched_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().vc_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 -- interpreter shutdown
+            pass
+
+    def admit(self, req: int, kv_full_bytes: float) -> Optional[int]:
+        """The reserved verify iteration, or None when nothing fits now."""
+        out = ctypes.c_int64()
+        rc = lib().vc_sched_admit(self._h, req, kv_full_bytes, ctypes.byref(out))
+        if rc == VC_EAGAIN:
+            return None
+        _check(rc)
+        return int(out.value)
+
+    def advance(self):
+        _check(lib().vc_sched_advance(self._h))
+
+    @property
+    def now(self) -> int:
+        return int(lib().vc_sched_now(self._h))
+
+    def ring(self, i: int):
+        a, b = ctypes.c_double(), ctypes.c_double()
+        _check(lib().vc_sched_ring(self._h, i, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def due(self, cap: int = 1024):
+        r = (ctypes.c_int32 * cap)()
+        v = (ctypes.c_int32 * cap)()
+        nr, nv = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().vc_sched_due(self._h, cap, r, ctypes.byref(nr), v, ctypes.byref(nv)))
+        return list(r[:nr.value]), list(v[:nv.value])
