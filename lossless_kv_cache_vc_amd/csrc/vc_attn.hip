@@ -1074,7 +1074,7 @@ __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) 
 //   scores   q.k^ = sum_c code_c (s_c q_c) + sum_c z_c q_c       (key scale/zero per channel)
 //   outputs  sum_t p_t v^_t,c = sum_t code_t,c (s_t,g p_t) + sum_t z_t,g p_t   (value per token)
 // so the per-element work is only expanding 2- or 4-bit codes to exact fp16 (one and-or per
-// pair, see pair_at).  Every product runs on 16x16x32 fp16 MFMA, the bias terms included: with
+// pair, see Expand).  Every product runs on 16x16x32 fp16 MFMA, the bias terms included: with
 // an A operand that is the same for every row (the zeros of the lane's channels or tokens, or the
 // negated expansion offsets), one MFMA sums over all 32 keys of the k-step, so the bias of row n
 // lands in every output row of column n without cross-lane sums.  Key biases initialise the score
@@ -1130,28 +1130,36 @@ __device__ __forceinline__ void ring_piece(const uint8_t* src, uint8_t* dst, int
 //          at bits 2 and 6, a right rotation by 6 does the same for pairs 2 and 3: offsets 256,
 //          16, 256, 16.
 // Bits rotated across a half boundary land outside every mask.
-// One v_and_or_b32 per pair: the mask comes from an SGPR and the exponent from a VGPR, since a
-// VOP3 instruction of this architecture takes no literal operand (the compiler would otherwise
-// split it into an and and an or with literals).
-__device__ __forceinline__ uint32_t pair_at(uint32_t x, int p, int bits) {
-  const uint32_t mask = (((1u << bits) - 1u) << p) * 0x00010001u;
-  const uint32_t magic = ((uint32_t)(25 - p) << 10) * 0x00010001u;
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-  return r;
-}
-
-// the 4 pairs (8 codes) of 2-bit word `w` selected by `hi` (0: pairs 0-3, 1: pairs 4-7)
-__device__ __forceinline__ u32x4 expand_2bit(uint32_t w, int hi) {
-  const uint32_t x = __builtin_rotateright32(w, hi ? 6 : 30);
-  return u32x4{pair_at(x, 2, 2), pair_at(x, 4, 2), pair_at(x, 6, 2), pair_at(x, 8, 2)};
-}
-
-// the 4 pairs (8 codes) of 4-bit word `w`
-__device__ __forceinline__ u32x4 expand_4bit(uint32_t w) {
-  const uint32_t x0 = __builtin_rotateright32(w, 30), x1 = __builtin_rotateright32(w, 6);
-  return u32x4{pair_at(x0, 2, 4), pair_at(x0, 6, 4), pair_at(x1, 2, 4), pair_at(x1, 6, 4)};
-}
+// Masks and exponents of the expansion, per pair position, held in registers: as literals the
+// compiler would split each and-or into an and and an or (a VOP3 instruction of this
+// architecture takes no literal operand).  The empty asm statements only make the values opaque
+// so that they stay in an SGPR (mask) and a VGPR (exponent); they emit no instruction.
+template <int BITS>
+struct Expand {
+  uint32_t mask[4], magic[4];
+  __device__ __forceinline__ Expand() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // 2-bit: positions 2, 4, 6, 8; 4-bit: positions 2, 6, 2, 6
+      const int p = BITS == 2 ? 2 + 2 * i : 2 + 4 * (i & 1);
+      mask[i] = (((1u << BITS) - 1u) << p) * 0x00010001u;
+      magic[i] = ((uint32_t)(25 - p) << 10) * 0x00010001u;
+      asm volatile("" : "+s"(mask[i]));
+      asm volatile("" : "+v"(magic[i]));
+    }
+  }
+  __device__ __forceinline__ uint32_t pair(uint32_t x, int i) const { return (x & mask[i]) | magic[i]; }
+  // 2-bit: the 4 pairs (8 codes) of word `w` selected by `hi` (0: pairs 0-3, 1: pairs 4-7)
+  __device__ __forceinline__ u32x4 bits2(uint32_t w, int hi) const {
+    const uint32_t x = __builtin_rotateright32(w, hi ? 6 : 30);
+    return u32x4{pair(x, 0), pair(x, 1), pair(x, 2), pair(x, 3)};
+  }
+  // 4-bit: the 4 pairs (8 codes) of word `w`
+  __device__ __forceinline__ u32x4 bits4(uint32_t w) const {
+    const uint32_t x0 = __builtin_rotateright32(w, 30), x1 = __builtin_rotateright32(w, 6);
+    return u32x4{pair(x0, 0), pair(x0, 1), pair(x1, 2), pair(x1, 3)};
+  }
+};
 
 // negated offsets of the expanded pairs, as an fp16 A operand (the same for every row)
 template <int BITS>
@@ -1255,25 +1263,14 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 #pragma unroll
   for (int i = 0; i < NGQ; ++i) vb[i] = f32x4{};
   const u32x4 noff = neg_offsets<BITS>();
+  const Expand<BITS> ex;
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
   const int vtok0 = 8 * (kg & 1), vpage = kg >> 1;  // this lane's 8 tokens of a pair
 
-  for (int k = 0; k < mine; ++k) {
-    wait_ahead<R::kLoads, STG - 2>(min(STG - 2, mine - 1 - k));
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (k + STG - 1 < mine) issue(k + STG - 1, __builtin_amdgcn_readfirstlane(pf0), __builtin_amdgcn_readfirstlane(pf1));
-    pair_ids(k + STG, pf0, pf1);
-
-    const uint8_t* slot = ring + (k % STG) * R::kSlot;
-    const int pp = w + NW * k;
-    // ---- page validity (full pairs need no masking)
-    const int ip0 = 2 * pp;
-    const int v0 = ids[ip0] < 0 ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0));
-    // the odd page's keys use the group parameters stored with the even page
-    const int v1 = (ids[ip0] < 0 || ids[ip0 + 1] < 0) ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0 + 1));
-    const bool full = v0 == kBlock && v1 == kBlock;
-
+  // Scores of the pair in `slot` (biases included), and the softmax and value products of pair k
+  // given its scores.
+  auto scores = [&](const uint8_t* slot, f32x4 (&s_acc)[2]) {
     // ---- key side: q' = q * scale (per channel); bias of column n = sum_c (z_c q_c - off_c q'_c)
     u32x4 qs[NS];
     f32x4 kb = f32x4{};
@@ -1289,7 +1286,6 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     // ---- scores S^T for the pair's two 16-key halves: A-operand row m is key (page m / 8,
     // token 8 ((m >> 2) & 1) + 4 b + (m & 3)), so lane (n, kg) ends with tokens 8 (kg & 1) + 4 b + i
     // of page kg / 2 -- exactly the B operand of the value product
-    f32x4 s_acc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int tk = 8 * ((n >> 2) & 1) + 4 * b + (n & 3);
@@ -1301,10 +1297,19 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         // the lane's channels 8s .. 8s + 7
-        const u32x4 av = BITS == 2 ? expand_2bit(words[s >> 1], s & 1) : expand_4bit(words[s]);
+        const u32x4 av = BITS == 2 ? ex.bits2(words[s >> 1], s & 1) : ex.bits4(words[s]);
         s_acc[b] = mfma16<true>(av, qs[s], s_acc[b]);
       }
     }
+  };
+  auto consume = [&](int k, const uint8_t* slot, const f32x4 (&s_acc)[2]) {
+    const int pp = w + NW * k;
+    // ---- page validity (full pairs need no masking)
+    const int ip0 = 2 * pp;
+    const int v0 = ids[ip0] < 0 ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0));
+    // the odd page's keys use the group parameters stored with the even page
+    const int v1 = (ids[ip0] < 0 || ids[ip0 + 1] < 0) ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0 + 1));
+    const bool full = v0 == kBlock && v1 == kBlock;
     // ---- online softmax over this lane's 8 keys
     float sv[8];
 #pragma unroll
@@ -1361,10 +1366,20 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
         const int dd = 16 * db + n;
         const uint32_t* vw = reinterpret_cast<const uint32_t*>(vcodes + dd * (kBlock * BITS / 8));
         // the lane's tokens vtok0 .. vtok0 + 7 of channel dd
-        const u32x4 av = BITS == 2 ? expand_2bit(vw[0], kg & 1) : expand_4bit(vw[kg & 1]);
+        const u32x4 av = BITS == 2 ? ex.bits2(vw[0], kg & 1) : ex.bits4(vw[kg & 1]);
         acc_o[db] = mfma16<true>(av, pv, acc_o[db]);
       }
     }
+  };
+  for (int k = 0; k < mine; ++k) {
+    wait_ahead<R::kLoads, STG - 2>(min(STG - 2, mine - 1 - k));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (k + STG - 1 < mine) issue(k + STG - 1, __builtin_amdgcn_readfirstlane(pf0), __builtin_amdgcn_readfirstlane(pf1));
+    pair_ids(k + STG, pf0, pf1);
+    const uint8_t* slot = ring + (k % STG) * R::kSlot;
+    f32x4 s_acc[2];
+    scores(slot, s_acc);
+    consume(k, slot, s_acc);
   }
 
   // the value bias joins the outputs before any pair that rescales without it
