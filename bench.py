@@ -209,7 +209,10 @@ def main():
 
     def roof(kind):
         if kind == "verify":
-            achieved, per_launch, name, role = verify_gbps, v_bytes, "verify_kernel<128>", "verify"
+            # a verify-only launch of more than 128 query rows per kv head runs the wide kernel
+            wide = max(r.x for r in cfg.reqs) * cfg.G > 128
+            name = "verify_wide_kernel<128>" if wide else "verify_kernel<128>"
+            achieved, per_launch, role = verify_gbps, v_bytes, "verify"
         else:
             achieved, per_launch, name, role = draft_gbps, sum(d_bytes) / x, draft_name, draft_role
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

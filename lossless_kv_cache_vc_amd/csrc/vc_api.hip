@@ -84,14 +84,35 @@ static PoolDev to_dev(const vc_pool& p) {
   return d;
 }
 
-static int auto_chunk(const vc_shape* s, int nreq, const vc_req* reqs) {
+// Verify-only launches whose largest request has more than 128 query rows (rows x G) per
+// (layer, kv head) use the wide verify: those rows are cut into as few groups of at most
+// 32 * kWideMaxWaves as possible, and the work-group has one wave per 32 rows of a group.
+static int plan_vwaves(int G, int nreq, const vc_req* reqs) {
+  int64_t maxrows = 0;
+  for (int i = 0; i < nreq; ++i) {
+    if (reqs[i].kind != VC_VERIFY) return 0;
+    maxrows = std::max<int64_t>(maxrows, (int64_t)reqs[i].rows * G);
+  }
+  if (maxrows <= 128 || maxrows > (1 << 20)) return 0;  // (bad row counts are rejected later)
+  const int64_t cap = 32 * kWideMaxWaves;
+  const int64_t groups = (maxrows + cap - 1) / cap;
+  const int64_t per = (maxrows + groups - 1) / groups;
+  return (int)((per + 31) / 32);
+}
+
+static int64_t row_groups(const vc_req& r, int G, int vwaves) {
+  if (r.kind != VC_VERIFY) return 1;
+  const int64_t per = vwaves ? 32 * vwaves : 128;
+  return ((int64_t)r.rows * G + per - 1) / per;
+}
+
+static int auto_chunk(const vc_shape* s, int nreq, const vc_req* reqs, int vwaves) {
   // aim for about 2048 work items (8 per CU) so the 256 CUs see several waves of work-groups
   const int G = s->num_q_heads / s->num_kv_heads;
   int64_t total = 0;
   for (int i = 0; i < nreq; ++i) {
     const int pages = (reqs[i].ctx_len + kBlock - 1) / kBlock;
-    const int nrg = reqs[i].kind == VC_VERIFY ? (reqs[i].rows * G + 127) / 128 : 1;
-    total += (int64_t)s->num_layers * s->num_kv_heads * nrg * pages;
+    total += (int64_t)s->num_layers * s->num_kv_heads * row_groups(reqs[i], G, vwaves) * pages;
   }
   int64_t chunk = (total + 2047) / 2048;
   chunk = std::max<int64_t>(16, (chunk + 3) / 4 * 4);
@@ -111,7 +132,8 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   memset(args, 0, sizeof(*args));
   for (int i = 0; i < npools; ++i) args->pools[i] = to_dev(pools[i]);
   std::vector<char> pool_used(npools, 0);
-  const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs);
+  const int vwaves = plan_vwaves(G, nreq, reqs);
+  const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs, vwaves);
   int64_t items = 0, part = 0;
   plan->any_split = 0;
   for (int i = 0; i < nreq; ++i) {
@@ -160,7 +182,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
     d.kind = r.kind;
     const int target = std::min(chunk, kMaxChunkPages);
     d.chunk_pages = split_context(pages, target, &d.nsplit);
-    d.nrg = r.kind == VC_VERIFY ? (r.rows * G + 127) / 128 : 1;
+    d.nrg = (int32_t)row_groups(r, G, vwaves);
     d.item_base = (int32_t)items;
     items += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * d.nrg;
     if (d.nsplit > 1) {
@@ -181,7 +203,9 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   args->nitems = (int)items;
   args->nitems_pad = (int)((items + 7) / 8 * 8);
   args->scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  args->vwaves = vwaves;
   plan->nitems = (int)items;
+  plan->vwaves = vwaves;
   plan->part_floats = part;
   plan->head_dim = D;
   return VC_OK;
@@ -226,7 +250,8 @@ size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req*
   if (check_shape(shape)) return 0;
   if (num_reqs <= 0 || num_reqs > VC_MAX_REQS || !reqs) return 0;
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  const int chunk = split_pages > 0 ? split_pages : auto_chunk(shape, num_reqs, reqs);
+  const int chunk =
+      split_pages > 0 ? split_pages : auto_chunk(shape, num_reqs, reqs, plan_vwaves(G, num_reqs, reqs));
   if (chunk <= 0) return 0;
   size_t floats = 0;
   for (int i = 0; i < num_reqs; ++i) {

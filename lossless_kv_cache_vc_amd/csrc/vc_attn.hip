@@ -254,6 +254,15 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One ring load: 16 bytes per lane from a wave-uniform page base plus a 32-bit lane offset into
+// LDS.  The empty asm keeps the offset's zero-extension beside the load, so the compiler selects
+// the scalar-base form of global_load_lds (one VGPR per lane offset) instead of hoisting a 64-bit
+// address per offset out of the loop.
+__device__ __forceinline__ void ring_load(const uint8_t* page, uint32_t off, uint8_t* dst) {
+  asm volatile("" : "+v"(off));
+  __builtin_amdgcn_global_load_lds(page + off, (lds_ptr_t)dst, 16, 0, kNontemporal);
+}
+
 struct VPage {
   int kind;   // 0 context, 1 drafted block, 2 none
   int valid;  // tokens present
@@ -469,38 +478,43 @@ __device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it
   verify_consume<D, MASK>(it, vs, smem, t, vst, s_cur);
 }
 
+// Byte offset inside a K or V page of this lane's part of ring load i.  The LDS side of
+// global_load_lds is lane-linear, so the XOR swizzle of the ring is applied by choosing which
+// global 16-byte chunk each lane fetches: keys by swz_k of the key row, values (pages stored d
+// major, 16 tokens of one channel per 32 bytes) by bit 3 of the channel.
 template <int D>
-__device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
-  using R = VRing<D>;
-  using VS = VerifyState<D>;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const int rb = w & 3;
+__device__ __forceinline__ uint32_t ring_lane_off(bool key, int lane, int i) {
+  if (key) {
+    constexpr int CPR = D / 8;           // 16-byte chunks per key row
+    constexpr int RPI = 1024 / (2 * D);  // key rows per load
+    const int tk = RPI * i + lane / CPR, sl = lane % CPR;
+    return tk * (2 * D) + ((sl ^ swz_k<D>(tk)) * 16);
+  }
+  const int dd = 32 * i + (lane >> 1), sl = lane & 1;
+  return dd * 32 + ((sl ^ ((dd >> 3) & 1)) * 16);
+}
+
+// Start of a verify item (both verify work-group shapes): the query registers of `row`, the
+// unit of every context page into LDS at `ids`, and the tile counts.  Returns with the
+// work-group synchronised and this wave's vector memory loads complete, so the ring loop's vmcnt
+// waits count ring loads only.
+template <int D>
+__device__ __forceinline__ void verify_begin(const AttnArgs& a, const ItemCtx& it, int row, VerifyState<D>& vs,
+                                             int32_t* units, int nthreads) {
+  constexpr int NS = VerifyState<D>::NS;
+  const int tid = threadIdx.x;
   const ReqDev& rq = it.rq;
   const int G = a.G;
-  const int row = rg * 128 + 32 * rb + n;
   const bool row_ok = row < it.rows_total;
   const int tok = row_ok ? row / G : 0;
-
-  VS vs;
-  vs.kh = w >> 2;
-  vs.n = n;
-  vs.h = h;
-  vs.kwave = w < 4;
-  vs.ps = w & 3;
-  vs.wave_on = rg * 128 + 32 * rb < it.rows_total;
   vs.qpos = rq.q0 + tok;
   vs.sc = a.scale_log2;
   {
     const uint16_t* qp = a.q + ((((int64_t)rq.slot * a.L + it.l) * a.xmax + rq.q0 + tok) * a.Hq +
                                 it.g * G + (row_ok ? row % G : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < VS::NS; ++s) vs.qreg[s] = row_ok ? ld16(qp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) vs.qreg[s] = row_ok ? ld16(qp + 16 * s + 8 * vs.h) : u32x4{0, 0, 0, 0};
   }
-
-  // unit index of every context page of the item, and the first invalid one
-  int32_t* units = reinterpret_cast<int32_t*>(smem + R::kIds);
   int* first_bad = units + kMaxChunkPages;
   {
     const PoolDev& pl = it.pool;
@@ -509,37 +523,49 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
     if (tid == 0) *first_bad = it.nctx;
     __syncthreads();
     const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
-    for (int i = tid; i < it.nctx; i += kVThreads) {
+    for (int i = tid; i < it.nctx; i += nthreads) {
       const int phys = pt[i];
       const bool ok = phys >= 0 && phys < pl.nblk;
       units[i] = ok ? (int32_t)(vs.dummy_unit + (int64_t)phys * a.Hkv) : -1;
       if (!ok) atomicMin(first_bad, i);
     }
   }
-  // the query registers and page table reads are complete before the first ring load is
-  // issued, so the loop's vmcnt waits cover ring loads only
   wait_vmem<0>();
   __syncthreads();
   vs.units = units;
   vs.ntiles = (it.npages + 3) >> 2;
-  const int ntiles = vs.ntiles;
   const int nfull = min(it.nctx, max(0, (rq.ctx_len - kBlock * it.p_lo) / kBlock));
   vs.t_full = min(nfull, *first_bad) >> 2;  // leading tiles of 4 full, valid context pages
-
-  // Per-lane offsets.  Loads: the LDS side of global_load_lds is lane-linear, so the XOR
-  // swizzle of the ring is applied by choosing which global chunk each lane fetches.
 #pragma unroll
-  for (int i = 0; i < VS::NL; ++i) {
-    if (vs.kwave) {
-      constexpr int CPR = D / 8;           // 16-byte chunks per key row
-      constexpr int RPI = 1024 / (2 * D);  // key rows per load
-      const int tk = RPI * i + lane / CPR, sl = lane % CPR;
-      vs.lane_off[i] = tk * (2 * D) + ((sl ^ swz_k<D>(tk)) * 16);
-    } else {
-      const int dd = 32 * i + (lane >> 1), sl = lane & 1;
-      vs.lane_off[i] = dd * 32 + ((sl ^ ((dd >> 3) & 1)) * 16);
-    }
-  }
+  for (int i = 0; i < VerifyState<D>::ND; ++i) vs.acc_o[i] = f32x16{};
+  vs.m_run = -INFINITY;
+  vs.l_run = 0.f;
+}
+
+template <int D>
+__device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
+  using R = VRing<D>;
+  using VS = VerifyState<D>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int rb = w & 3;
+  const int row = rg * 128 + 32 * rb + n;
+  const bool row_ok = row < it.rows_total;
+
+  VS vs;
+  vs.kh = w >> 2;
+  vs.n = n;
+  vs.h = h;
+  vs.kwave = w < 4;
+  vs.ps = w & 3;
+  vs.wave_on = rg * 128 + 32 * rb < it.rows_total;
+  int32_t* units = reinterpret_cast<int32_t*>(smem + R::kIds);
+  verify_begin<D>(a, it, row, vs, units, kVThreads);
+  const int ntiles = vs.ntiles;
+
+#pragma unroll
+  for (int i = 0; i < VS::NL; ++i) vs.lane_off[i] = ring_lane_off<D>(vs.kwave, lane, i);
   {
     const int key = 32 * vs.kh + key_of_m32(n);
     const int ksw = swz_k<D>(key);
@@ -547,10 +573,6 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
     for (int s = 0; s < VS::NS; ++s) vs.koff[s] = key * (2 * D) + (((2 * s + h) ^ ksw) * 16);
     vs.voff = R::kV0 + 2 * vs.kh * R::kPage + n * 32 + ((h ^ ((n >> 3) & 1)) * 16);
   }
-#pragma unroll
-  for (int i = 0; i < VS::ND; ++i) vs.acc_o[i] = f32x16{};
-  vs.m_run = -INFINITY;
-  vs.l_run = 0.f;
 
   // prologue: K(0..3) and V(0..3) into stages 0..3; scores of tile 0
   const int kpro = min(ntiles, 4);
@@ -623,6 +645,193 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
     }
   if (partial && h == 0) {
     dst[D] = M;
+    dst[D + 1] = l_tot;
+  }
+}
+
+// ------------------------------------------------------------------ wide verify
+// Verify launches with more than 128 query rows per (layer, kv head) (x * G > 128, e.g. G = 8
+// and x = 40) take up to 384 rows in one work item, one wave per 32 rows (up to 12 waves, 3 per
+// SIMD), so a unit's K/V pages stream through a CU once for all its rows instead of once per
+// 128-row group.  Each wave scores both 32-key halves of every 64-key tile and folds each half
+// into its online softmax in turn; no key halves are merged at the end.  K and V pages go into
+// a 4-stage ring each (stages hold 64-key tiles; tile t + 3 is loaded while tile t is
+// consumed).  The 8 pages of a tile are dealt over the waves as ring slots, slot s < 4 being key
+// page s and slot s >= 4 value page s - 4: wave w loads slots w and w + waves (those below 8).
+constexpr int kWStages = 4;
+constexpr int kWThreads = 64 * kWideMaxWaves;
+
+template <int D>
+struct WRing {
+  static constexpr int kPage = kBlock * D * 2;
+  static constexpr int kTile = 4 * kPage;
+  static constexpr int kV0 = kWStages * kTile;  // value stages after the key stages
+  static constexpr int kIds = 2 * kWStages * kTile;
+  static constexpr int kBytes = kIds + kMaxChunkPages * 4 + 16;
+  static constexpr int kLoads = kPage / 1024;
+};
+// the value product (verify_consume) addresses value stage j at kV0 + j * kTile of either ring
+static_assert(WRing<128>::kV0 == VRing<128>::kV0 && WRing<64>::kV0 == VRing<64>::kV0, "value stage base");
+static_assert(WRing<128>::kTile == VRing<128>::kTileK && WRing<64>::kTile == VRing<64>::kTileK, "stage size");
+
+// ring_lane_off(key, lane, i) == ring_lane_off(key, lane, 0) ^ (i * step): load i of a page
+// covers the next 1 KB (keys: 4 rows of 256 bytes or 8 of 128, the row swizzle advancing by
+// 4 or 8 with them; values: 32 channels of 32 bytes)
+__device__ __forceinline__ uint32_t ring_load_step(bool key) { return key ? 1088u : 1024u; }
+
+struct WideLoads {
+  int nslot;  // ring slots this wave loads: 0, 1 or 2 (the planner uses at least 5 waves)
+  int s0, s1;
+  int pf0, pf1;         // units of the pages the slots load next (read from LDS a tile early)
+  uint32_t off0, off1;  // lane offsets of each slot's load 0 (see ring_load_step)
+};
+
+// Unit of context page ip of the item, -1 past the context (drafted block or nothing).
+__device__ __forceinline__ int unit_at(const int32_t* units, const ItemCtx& it, int ip) {
+  return ip < it.nctx ? units[ip] : -1;
+}
+
+// Issue ring slot `slot` of tile t into stage `stage`.
+template <int D>
+__device__ __forceinline__ void wide_issue(const AttnArgs& a, const ItemCtx& it, const VerifyState<D>& vs,
+                                           uint8_t* smem, int slot, uint32_t off, int t, int stage, int unit) {
+  using R = WRing<D>;
+  const int ps = slot & 3;
+  const int ip = 4 * t + ps;
+  const bool key = slot < 4;
+  const uint8_t* page = key ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip, unit)
+                            : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip, unit);
+  uint8_t* dst = smem + (key ? 0 : R::kV0) + stage * R::kTile + ps * R::kPage;
+  const uint32_t step = ring_load_step(key);
+  asm volatile("" : "+v"(off));  // derive the load offsets here, not as registers held in the loop
+#pragma unroll
+  for (int i = 0; i < R::kLoads; ++i) ring_load(page, off ^ (i * step), dst + i * 1024);
+}
+
+// wait until this wave's ring loads of the current tile have landed, with `ahead` (0..2) later
+// tiles' loads still in flight
+template <int D>
+__device__ __forceinline__ void wide_wait(int nslot, int ahead) {
+  constexpr int L = WRing<D>::kLoads;
+  if (nslot == 1) {
+    if (ahead >= 2) wait_vmem<2 * L>();
+    else if (ahead == 1) wait_vmem<L>();
+    else wait_vmem<0>();
+  } else if (nslot == 2) {
+    if (ahead >= 2) wait_vmem<4 * L>();
+    else if (ahead == 1) wait_vmem<2 * L>();
+    else wait_vmem<0>();
+  }
+}
+
+// S^T for key half KH of the tile in key stage `st`.  kx = key row * 2D | ((h ^ swz_k) << 4):
+// the XOR-swizzled chunk (2 s + h) ^ swz_k of the row is kx ^ (32 s), the row offset having
+// zero low bits.
+template <int D, int KH>
+__device__ __forceinline__ f32x16 wide_scores(const uint8_t* smem, int st, uint32_t kx, const u32x4* qreg) {
+  constexpr int NS = VerifyState<D>::NS;
+  const uint8_t* kst = smem + st * WRing<D>::kTile + KH * 32 * (2 * D);
+  u32x4 av[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) av[s] = ld16(kst + (kx ^ (32u * s)));
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(av[s]), as_bf(qreg[s]), acc, 0, 0, 0);
+  return acc;
+}
+
+// One tile: wait for tile t, refill the stage freed by tile t - 1 with tile t + 3, then both
+// key halves of tile t, one after the other.  STC >= 0: t % 4 == STC known at compile time.
+template <int D, int STC, bool MASK>
+__device__ __forceinline__ void wide_step(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs,
+                                          WideLoads& ld, uint8_t* smem, int t, uint32_t kx, uint32_t voff0) {
+  const int st = STC >= 0 ? STC : (t & (kWStages - 1));
+  const int ntiles = vs.ntiles;
+  wide_wait<D>(ld.nslot, min(2, ntiles - 1 - t));
+  ring_barrier();
+  if (t + 3 < ntiles) {
+    const int sn = (st + 3) & (kWStages - 1);
+    if (ld.nslot >= 1) wide_issue<D>(a, it, vs, smem, ld.s0, ld.off0, t + 3, sn, ld.pf0);
+    if (ld.nslot == 2) wide_issue<D>(a, it, vs, smem, ld.s1, ld.off1, t + 3, sn, ld.pf1);
+  }
+  ld.pf0 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s0 & 3));
+  ld.pf1 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s1 & 3));
+  if (!vs.wave_on) return;
+  asm volatile("" : "+v"(kx));  // the 8 operand offsets kx ^ 32 s are derived here, not held
+  vs.kh = 0;
+  vs.voff = voff0;
+  verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 0>(smem, st, kx, vs.qreg));
+  vs.kh = 1;
+  vs.voff = voff0 + 2 * WRing<D>::kPage;
+  verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 1>(smem, st, kx, vs.qreg));
+}
+
+template <int D>
+__device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
+  using R = WRing<D>;
+  using VS = VerifyState<D>;
+  const int nw = a.vwaves;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int rows0 = rg * 32 * nw + 32 * w;  // first row of this wave
+  const int row = rows0 + n;
+  const bool row_ok = row < it.rows_total;
+
+  VS vs;
+  vs.n = n;
+  vs.h = h;
+  vs.wave_on = rows0 < it.rows_total;
+  int32_t* units = reinterpret_cast<int32_t*>(smem + R::kIds);
+  verify_begin<D>(a, it, row, vs, units, 64 * nw);
+  const int ntiles = vs.ntiles;
+
+  WideLoads ld;
+  ld.s0 = w;
+  ld.s1 = w + nw;
+  ld.nslot = (ld.s0 < 8) + (ld.s1 < 8);
+  ld.off0 = ring_lane_off<D>(ld.s0 < 4, lane, 0);
+  ld.off1 = ring_lane_off<D>(ld.s1 < 4, lane, 0);
+  const int key = key_of_m32(n);
+  const uint32_t kx = key * (2 * D) | ((h ^ swz_k<D>(key)) << 4);
+  const uint32_t voff0 = R::kV0 + n * 32 + ((h ^ ((n >> 3) & 1)) * 16);
+
+  // prologue: tiles 0..2 into stages 0..2
+  const int kpro = min(ntiles, 3);
+  for (int j = 0; j < kpro; ++j) {
+    if (ld.nslot >= 1) wide_issue<D>(a, it, vs, smem, ld.s0, ld.off0, j, j, unit_at(units, it, 4 * j + (ld.s0 & 3)));
+    if (ld.nslot == 2) wide_issue<D>(a, it, vs, smem, ld.s1, ld.off1, j, j, unit_at(units, it, 4 * j + (ld.s1 & 3)));
+  }
+  ld.pf0 = unit_at(units, it, 12 + (ld.s0 & 3));
+  ld.pf1 = unit_at(units, it, 12 + (ld.s1 & 3));
+
+  int t = 0;
+  for (; t + 3 < vs.t_full; t += 4) {
+    wide_step<D, 0, false>(a, it, vs, ld, smem, t, kx, voff0);
+    wide_step<D, 1, false>(a, it, vs, ld, smem, t + 1, kx, voff0);
+    wide_step<D, 2, false>(a, it, vs, ld, smem, t + 2, kx, voff0);
+    wide_step<D, 3, false>(a, it, vs, ld, smem, t + 3, kx, voff0);
+  }
+  for (; t < vs.t_full; ++t) wide_step<D, -1, false>(a, it, vs, ld, smem, t, kx, voff0);
+  for (; t < ntiles; ++t) wide_step<D, -1, true>(a, it, vs, ld, smem, t, kx, voff0);
+
+  if (!vs.wave_on) return;
+  // the row's keys are split over the two 32-lane halves (tokens 8 h .. 8 h + 7 of each page)
+  const float l_tot = half_swap_sum(vs.l_run);
+  if (!row_ok) return;
+  bool partial;
+  float* dst = out_row<D>(a, it, row, &partial);
+  const float inv = partial ? 1.f : (l_tot > 0.f ? 1.f / l_tot : 0.f);
+#pragma unroll
+  for (int db = 0; db < VS::ND; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 o = f32x4{vs.acc_o[db][4 * q], vs.acc_o[db][4 * q + 1], vs.acc_o[db][4 * q + 2],
+                            vs.acc_o[db][4 * q + 3]} * inv;
+      *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q + 4 * h) = o;
+    }
+  if (partial && h == 0) {
+    dst[D] = vs.m_run;
     dst[D + 1] = l_tot;
   }
 }
@@ -1453,6 +1662,16 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(const AttnArgs a) {
   verify_item<D>(a, it, rg, smem);
 }
 
+// Verify items only, wide work-groups (a.vwaves waves of 32 rows).
+template <int D>
+__global__ __launch_bounds__(kWThreads) void verify_wide_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[WRing<D>::kBytes];
+  ItemCtx it;
+  int rg;
+  if (!decode_item(a, &it, &rg)) return;
+  verify_wide_item<D>(a, it, rg, smem);
+}
+
 // Draft items only, one pool (so one bit width) per launch: 4 waves that split the item's keys.
 template <int D>
 __global__ __launch_bounds__(kDThreads) void draft_bf16_kernel(const AttnArgs a) {
@@ -1535,7 +1754,15 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
   const dim3 grid(args.nitems_pad);
   bool has_v = false, has_d = false;
   for (int i = 0; i < args.nreq; ++i) (args.reqs[i].kind == VC_VERIFY ? has_v : has_d) = true;
-  if (head_dim == 128) {
+  if (args.vwaves) {
+    // verify-only launches; the kernel deals the 8 ring slots of a tile over its waves, at most
+    // two per wave
+    if (has_d || args.vwaves < 4 || args.vwaves > kWideMaxWaves)
+      return fail(VC_EINVAL, "internal: bad wide verify plan");
+    const dim3 block(64 * args.vwaves);
+    if (head_dim == 128) hipLaunchKernelGGL(verify_wide_kernel<128>, grid, block, 0, stream, args);
+    else hipLaunchKernelGGL(verify_wide_kernel<64>, grid, block, 0, stream, args);
+  } else if (head_dim == 128) {
     if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
     else if (has_v) hipLaunchKernelGGL(verify_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
     else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<128>, grid, dim3(kDThreads), 0, stream, args);

@@ -60,6 +60,8 @@ struct AttnArgs {
   float* part;
   int32_t L, Hq, Hkv, G, xmax, nreq, nitems, nitems_pad;
   float scale_log2;  // log2(e) / sqrt(d)
+  int32_t vwaves;    // verify work-group: 0 = 8 waves over 128-row groups; else that many
+                     // waves, one per 32 rows, over groups of 32 * vwaves rows (wide verify)
   ReqDev reqs[kMaxReqs];
 };
 
@@ -68,6 +70,7 @@ static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit 4 KiB");
 // Plan an attention launch: fills reqs/nitems and returns workspace floats needed.
 struct Plan {
   int nitems = 0;
+  int vwaves = 0;  // wide verify waves (0: the 8-wave verify)
   int64_t part_floats = 0;
   int any_split = 0;
   int head_dim = 0;
@@ -76,6 +79,9 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
               int split_pages, AttnArgs* args, Plan* plan);
 
 int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_t stream);
+
+// Largest wide-verify work-group: 12 waves (3 per SIMD), 384 query rows.
+constexpr int kWideMaxWaves = 12;
 
 // Context pages of one work item are capped so that their block ids fit the kernels' LDS.
 constexpr int kMaxChunkPages = 2048;

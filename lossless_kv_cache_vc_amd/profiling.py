@@ -30,6 +30,7 @@ ATTN_SRC = os.path.join(PKG, "csrc", "vc_attn.hip")
 # kernel-name fragment -> role reported by the benchmark
 ROLES = {
     "verify_kernel<128>": "verify",
+    "verify_wide_kernel<128>": "verify",
     "draft_bf16_kernel<128>": "draft",
     "draft_kivi_kernel<128, 2>": "draft_kivi2",
     "draft_kivi_kernel<128, 4>": "draft_kivi4",

@@ -115,6 +115,42 @@ def test_verify_parity(name):
     print(f"{name} verify max-abs error {worst:.3e}")
 
 
+def wide_cfg(kind):
+    """Verify launches of more than 128 query rows (x * G) per (layer, kv head)."""
+    c4 = C.get("C4")
+    if kind == "g8_x17":    # 136 rows: 5 waves, three of which load two ring slots
+        return C.scaled(c4, L=1, B=2, n=900, x=17)
+    if kind == "g8_x64":    # 512 rows: two row groups of 256 (8 waves)
+        return C.scaled(c4, L=1, B=1, n=700, x=64)
+    if kind == "g16_d64":   # G = 16, d = 64: 24 * 16 = 384 rows (12 waves), and a request of 3 * 16
+        reqs = [C.Request(ctx_len=650, x=24, comp=C.COMP_DROP, recent=64, top=650 // 4),
+                C.Request(ctx_len=333, x=3, comp=C.COMP_DROP, recent=64, top=333 // 4)]
+        return C.Config("wide-g16-d64", 41, L=1, Hq=32, Hkv=2, d=64, reqs=reqs, wu_width=512,
+                        vocab=1024)
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind,split_pages", [("g8_x17", 0), ("g8_x17", 8), ("g8_x64", 0),
+                                              ("g16_d64", 0), ("g16_d64", 4)])
+def test_wide_verify_parity(kind, split_pages):
+    """Every output element of the wide verify work-groups (one wave per 32 rows, 5 to 12 waves)
+    against the oracle, unsplit and with context splits of 2 and 1 tiles (partials + merge)."""
+    require_gpu()
+    from lossless_kv_cache_vc_amd.harness import Workload
+    cfg = wide_cfg(kind)
+    print(f"wide verify {kind} split_pages={split_pages}", flush=True)
+    wl = Workload(cfg, build_compressed=False)
+    wl.run_verify(split_pages)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for r, req in enumerate(cfg.reqs):
+        for l in range(cfg.L):
+            want = ow.verify_out(cfg, r, l)
+            got = wl.out_v[r, l, :req.x].double().cpu().numpy()
+            worst = max(worst, assert_close(got, want, tight_tol(req.ctx_len), f"{kind} verify r={r} l={l}"))
+    print(f"{kind} verify max-abs error {worst:.3e}")
+
+
 @pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4"])
 def test_draft_parity(name):
     cfg, wl = built(name)
