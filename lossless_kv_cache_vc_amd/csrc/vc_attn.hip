@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kDWaves = 4;            // waves of a draft-only work-group (bf16 caches)
 constexpr int kDThreads = 64 * kDWaves;
-constexpr int kKWaves = 8;            // waves of a draft-only work-group (KIVI caches): two per SIMD
+constexpr int kKWaves = 12;           // waves of a draft-only work-group (KIVI caches): three per SIMD
 constexpr int kKThreads = 64 * kKWaves;
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
 
@@ -1321,10 +1321,7 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 template <int BYTES>
 __device__ __forceinline__ void ring_piece(const uint8_t* src, uint8_t* dst, int lane) {
   static_assert(BYTES % 16 == 0 && BYTES <= 1024, "ring piece");
-  if (BYTES == 1024 || lane < BYTES / 16) {
-    const void* s = src + 16 * lane;
-    __builtin_amdgcn_global_load_lds(s, (lds_ptr_t)dst, 16, 0, kNontemporal);
-  }
+  if (BYTES == 1024 || lane < BYTES / 16) ring_load(src, 16 * lane, dst);
 }
 
 // Code expansion.  A pair of codes sitting at mantissa bits [p, p + BITS) of both 16-bit
