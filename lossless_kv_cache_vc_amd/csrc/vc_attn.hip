@@ -6,15 +6,18 @@
 // softmax(q k^T / sqrt(d)) v (§Prerequisites, attention equation) over different key sets.
 //
 // One launch processes a list of work items; an item is (request, layer, kv head, context
-// split, row group).  Each work-group has 4 wave64s and takes one of two paths:
+// split, row group), and each work-group takes one item:
 //
 //  * verify path — the x*G query rows of a kv head are a dense block: each wave owns 32 rows,
-//    K/V tiles of 64 keys (4 pages) are staged through LDS (double buffered) and shared by the
-//    4 waves; S^T = K Q^T and O^T += V^T P^T use v_mfma_f32_32x32x16_bf16, so each lane holds
+//    K/V tiles of 64 keys (4 pages) stream from HBM straight into an LDS ring and are shared by
+//    all waves; S^T = K Q^T and O^T += V^T P^T use v_mfma_f32_32x32x16_bf16, so each lane holds
 //    one query row of both accumulators and the softmax needs only one cross-lane exchange.
-//  * draft path — G <= 16 rows: the waves split the keys of the item, load K/V pages straight
-//    into registers in MFMA operand order (v_mfma_f32_16x16x32_bf16, rows padded to 16),
-//    dequantise KIVI codes in registers, and merge the per-wave softmax states through LDS.
+//    verify_kernel (8 waves) covers up to 128 rows per item with two waves per row block, each
+//    taking one key half of every tile; verify_wide_kernel (5 to 12 waves) covers up to 384 rows
+//    per item with one wave per row block.
+//  * draft path — G <= 16 rows: the waves split the keys of the item, each wave streaming its
+//    own pages through a private LDS ring (v_mfma_f32_16x16x32, rows padded to 16); KIVI codes
+//    are expanded in registers, and the per-wave softmax states merge through LDS.
 //
 // Long contexts are split into chunks of pages; partial (max, sum, output) states go to the
 // workspace and a merge kernel combines them with log-sum-exp weights.
@@ -42,6 +45,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   t[0] = (__bf16)a;
   t[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, t);
+}
+
+// maximum of 16 floats as a chain the compiler turns into 3-input maxima (8 instructions)
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = fmaxf(fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int r = 3; r + 1 < 16; r += 2) m = fmaxf(fmaxf(m, v[r]), v[r + 1]);
+  return fmaxf(m, v[15]);
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
@@ -407,10 +418,7 @@ __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>
     for (int r = 0; r < 16; ++r)
       if (!vkey_visible(r < 8 ? p0 : p1, 8 * h + (r & 7), vs.qpos)) s_acc[r] = -INFINITY;
   }
-  float mloc = fmaxf(fmaxf(fmaxf(s_acc[0], s_acc[1]), fmaxf(s_acc[2], s_acc[3])),
-                     fmaxf(fmaxf(s_acc[4], s_acc[5]), fmaxf(s_acc[6], s_acc[7])));
-  mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s_acc[8], s_acc[9]), fmaxf(s_acc[10], s_acc[11])),
-                           fmaxf(fmaxf(s_acc[12], s_acc[13]), fmaxf(s_acc[14], s_acc[15]))));
+  float mloc = max16(s_acc);
   mloc = half_swap_max(mloc);
   const float sc = vs.sc;
   const float m_new = fmaxf(vs.m_run, mloc * sc);
