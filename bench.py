@@ -87,6 +87,24 @@ def cpu_baseline(cfg, budget_s: float):
                               f"timed and scaled by {n_units} units / {n_inst} instances")
 
 
+def stream_ceiling(args):
+    """The box's streaming-read peak (nontemporal vector reads of a contiguous 4 GiB buffer),
+    measured after the timed region; None when switched off."""
+    if args.no_stream_ceiling:
+        return None
+    from lossless_kv_cache_vc_amd import stream_probe
+    return stream_probe.measure(gib=4.0, reps=3)
+
+
+def with_ceiling(roof: dict, ceiling) -> dict:
+    """A roofline object plus its achieved rate as a fraction of the measured streaming-read
+    peak."""
+    if ceiling:
+        roof["ceiling_gbps"] = ceiling["read_gbps"]
+        roof["ceiling_frac"] = round(roof["achieved"] / ceiling["read_gbps"], 4)
+    return roof
+
+
 def bench_mixed(cfg, wl, args):
     """The ragged batch: one step is one launch over all requests, drafting and verifying."""
     import torch
@@ -114,6 +132,11 @@ def bench_mixed(cfg, wl, args):
                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.config, "mixed"),
                         "kernel": "mixed_kernel<128>", "algorithmic_bytes_per_launch": int(nbytes)},
            "breakdown_ms": {"launch": round(ms, 4)}}
+    ceiling = stream_ceiling(args)
+    if ceiling:
+        out["stream_ceiling"] = ceiling
+        out["pct_of_stream_ceiling"] = round(100 * gbps / ceiling["read_gbps"], 2)
+        with_ceiling(out["roofline"], ceiling)
     print(json.dumps(out), flush=True)
 
 
@@ -124,6 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip measuring the streaming-read ceiling after the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle work to time for the CPU baseline")
     ap.add_argument("--temperature", type=float, default=0.0,
@@ -257,6 +282,12 @@ def main():
         "accept": "greedy" if args.temperature <= 0 else f"rejection sampling, T = {args.temperature}",
         "bytes": {"verify": v_bytes, "draft_per_step_avg": int(sum(d_bytes) / x), "round": round_bytes},
     }
+    ceiling = stream_ceiling(args)
+    if ceiling:
+        out["stream_ceiling"] = ceiling
+        out["pct_of_stream_ceiling"] = round(100 * value_tbs * 1e3 / ceiling["read_gbps"], 2)
+        with_ceiling(out["roofline"], ceiling)
+        with_ceiling(out["roofline_verify"], ceiling)
     if not args.no_cpu_baseline:
         round_s, threads, sample = cpu_baseline(cfg, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(round_bytes / round_s / 1e12, 8), "unit": "TB/s",

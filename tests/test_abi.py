@@ -109,3 +109,15 @@ def test_sampling_entry_points_validate_on_host():
     _expect(vc.VC_EINVAL, lambda: acc(T=-1.0))
     _expect(vc.VC_EINVAL, lambda: acc(u=z))
     acc(n=0)
+
+
+def test_stream_probe_library_loads_and_rejects_bad_arguments():
+    """The streaming-read probe (a measurement library beside libvc) loads without a GPU and
+    refuses bad arguments before launching anything."""
+    from lossless_kv_cache_vc_amd import stream_probe as sp
+    L = sp.lib()
+    assert L.vcprobe_read(None, 16, 1, 0x3000, None) == -1
+    assert L.vcprobe_read(0x1000, 0, 1, 0x3000, None) == -1                      # nothing to read
+    assert L.vcprobe_read(0x1000, 24, 1, 0x3000, None) == -1                     # not 16-byte pieces
+    assert L.vcprobe_read(0x1000, 16, 0, 0x3000, None) == -1                     # no groups
+    assert L.vcprobe_read(0x1000, 16, 1, None, None) == -1
