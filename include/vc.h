@@ -88,7 +88,10 @@ typedef struct {
   int32_t bits;                /* 16, 2 or 4 */
   int32_t max_pages;           /* row stride of page_table */
   int64_t num_blocks;          /* nb: physical blocks per layer */
-  const int32_t* page_table;   /* (device) int32 [rows][max_pages]; -1 = no block */
+  const int32_t* page_table;   /* (device) int32 [rows][max_pages]; -1 = no block.  A context
+                                  page whose entry is -1 or >= num_blocks contributes no keys;
+                                  in a KIVI pool a missing even page 2j also removes page 2j+1
+                                  (the group's key parameters live in page 2j's block) */
   const void* k;               /* (device) see above */
   const void* v;               /* (device) */
   const void* k_sz;            /* (device) KIVI only, else NULL */

@@ -152,9 +152,15 @@ __device__ __forceinline__ PageRef page_ref(const AttnArgs& a, const ItemCtx& it
       const int wb = D * pl.bits / 8;  // bytes of one token row (keys) / one channel row (values)
       pr.k = pl.k + unit * (kBlock * wb);
       pr.v = pl.v + unit * (int64_t)(D * 2 * pl.bits);  // d channels x 16 tokens x bits / 8
-      int pe = p & ~1;
-      int phys_e = pl.page_table[(int64_t)rq.page_row * pl.max_pages + pe];
-      if (phys_e < 0 || phys_e >= pl.nblk) phys_e = phys;
+      // the key parameters of the page's 32-token group live in the block of its even page; a
+      // missing even page removes its odd partner too
+      const int pe = p & ~1;
+      const int phys_e = pe == p ? phys : pl.page_table[(int64_t)rq.page_row * pl.max_pages + pe];
+      if (phys_e < 0 || phys_e >= pl.nblk) {
+        pr.kind = 2;
+        pr.valid = 0;
+        return pr;
+      }
       int64_t unit_e = ((int64_t)it.l * pl.nblk + phys_e) * a.Hkv + it.g;
       pr.ksz = pl.ksz + unit_e * (D * 4);
       pr.vsz = pl.vsz + unit * (D / 32 * kBlock * 4);
