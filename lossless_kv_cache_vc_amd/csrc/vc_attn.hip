@@ -1312,12 +1312,15 @@ struct KRing {
   static constexpr int kOffV = 2 * kCodes;
   static constexpr int kOffKsz = 4 * kCodes;
   static constexpr int kOffVsz = kOffKsz + kKsz;
+  static constexpr int kParams = kKsz + 2 * kVsz;          // key and value parameters of a pair
   static constexpr int kSlot = (kOffVsz + 2 * kVsz + 1023) / 1024 * 1024;
-  static constexpr int kLoads = 7;                          // ring loads per slot
+  static constexpr int kCodeLoads = 2 * kCodes <= 1024 ? 1 : 2;  // loads of both pages' codes
+  static constexpr int kLoads = 2 * kCodeLoads + 1;              // ring loads per slot
   static constexpr int kIds = 144 * 1024 * D / 128;         // LDS offset of the page ids
   static constexpr int kStg0 = kIds / (NW * kSlot);
   static constexpr int kStg = kStg0 > 8 ? 8 : kStg0;        // slots per wave
-  static constexpr int kBytes = kIds + kMaxChunkPages * 4;
+  static constexpr int kBytes = kIds + kMaxChunkPages * 4 + 16;  // ids, then the first missing page
+  static_assert(kParams % 16 == 0 && kParams <= 1024, "the parameters of a pair are one load");
 };
 
 // wait until at most `ahead` slots (PER loads each) of this wave are still in flight
@@ -1336,6 +1339,21 @@ template <int BYTES>
 __device__ __forceinline__ void ring_piece(const uint8_t* src, uint8_t* dst, int lane) {
   static_assert(BYTES % 16 == 0 && BYTES <= 1024, "ring piece");
   if (BYTES == 1024 || lane < BYTES / 16) ring_load(src, 16 * lane, dst);
+}
+
+// ring loads of two pages' pieces of BYTES each, contiguous in LDS at dst: one load when both fit
+// in 1 KB (lanes split between the pages), else one per page
+template <int BYTES>
+__device__ __forceinline__ void ring_pair(const uint8_t* src0, const uint8_t* src1, uint8_t* dst, int lane) {
+  if constexpr (2 * BYTES <= 1024) {
+    const int o = 16 * lane;
+    const uint8_t* src = o < BYTES ? src0 + o : src1 + (o - BYTES);
+    if (2 * BYTES == 1024 || o < 2 * BYTES)
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, kNontemporal);
+  } else {
+    ring_piece<BYTES>(src0, dst, lane);
+    ring_piece<BYTES>(src1, dst + BYTES, lane);
+  }
 }
 
 // Code expansion.  A pair of codes sitting at mantissa bits [p, p + BITS) of both 16-bit
@@ -1433,12 +1451,17 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       qh[s] = bf16x8_to_f16x8(row_ok ? ld16(qp + draft_chan<D>(kg, s)) : u32x4{0, 0, 0, 0});
   }
   int32_t* ids = reinterpret_cast<int32_t*>(smem + R::kIds);
+  int* first_bad = ids + kMaxChunkPages;
   {
     const PoolDev& pl = it.pool;
+    if (tid == 0) *first_bad = it.nctx;
+    __syncthreads();
     const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
     for (int i = tid; i < it.nctx; i += 64 * NW) {
       const int phys = pt[i];
-      ids[i] = (phys < 0 || phys >= pl.nblk) ? -1 : phys;
+      const bool ok = phys >= 0 && phys < pl.nblk;
+      ids[i] = ok ? phys : -1;
+      if (!ok) atomicMin(first_bad, i);
     }
   }
   wait_vmem<0>();
@@ -1453,13 +1476,16 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     uint8_t* slot = ring + (k % STG) * R::kSlot;
     const int64_t u0 = unit0 + (int64_t)(id0 < 0 ? 0 : id0) * a.Hkv;
     const int64_t u1 = unit0 + (int64_t)(id1 < 0 ? 0 : id1) * a.Hkv;
-    ring_piece<R::kCodes>(pl.k + u0 * R::kCodes, slot, lane);
-    ring_piece<R::kCodes>(pl.k + u1 * R::kCodes, slot + R::kCodes, lane);
-    ring_piece<R::kCodes>(pl.v + u0 * R::kCodes, slot + R::kOffV, lane);
-    ring_piece<R::kCodes>(pl.v + u1 * R::kCodes, slot + R::kOffV + R::kCodes, lane);
-    ring_piece<R::kKsz>(pl.ksz + u0 * R::kKsz, slot + R::kOffKsz, lane);
-    ring_piece<R::kVsz>(pl.vsz + u0 * R::kVsz, slot + R::kOffVsz, lane);
-    ring_piece<R::kVsz>(pl.vsz + u1 * R::kVsz, slot + R::kOffVsz + R::kVsz, lane);
+    ring_pair<R::kCodes>(pl.k + u0 * R::kCodes, pl.k + u1 * R::kCodes, slot, lane);
+    ring_pair<R::kCodes>(pl.v + u0 * R::kCodes, pl.v + u1 * R::kCodes, slot + R::kOffV, lane);
+    // the group's key parameters and both pages' value parameters are contiguous in the slot:
+    // one load, each lane fetching its 16 bytes from the plane they come from
+    const int o = 16 * lane;
+    const uint8_t* src = o < R::kKsz ? pl.ksz + u0 * R::kKsz + o
+                         : o < R::kKsz + R::kVsz ? pl.vsz + u0 * R::kVsz + (o - R::kKsz)
+                                                 : pl.vsz + u1 * R::kVsz + (o - R::kKsz - R::kVsz);
+    if (R::kParams == 1024 || o < R::kParams)
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(slot + R::kOffKsz), 16, 0, kNontemporal);
   };
   auto pair_ids = [&](int k, int& id0, int& id1) {
     const int pp = w + NW * k;
@@ -1522,14 +1548,20 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       }
     }
   };
-  auto consume = [&](int k, const uint8_t* slot, const f32x4 (&s_acc)[2]) {
+  // FULL: the pair is known to be two full, present pages (no validity reads or masking)
+  auto consume = [&](int k, const uint8_t* slot, const f32x4 (&s_acc)[2], auto full_pair) {
+    constexpr bool FULL = decltype(full_pair)::value;
     const int pp = w + NW * k;
     // ---- page validity (full pairs need no masking)
-    const int ip0 = 2 * pp;
-    const int v0 = ids[ip0] < 0 ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0));
-    // the odd page's keys use the group parameters stored with the even page
-    const int v1 = (ids[ip0] < 0 || ids[ip0 + 1] < 0) ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0 + 1));
-    const bool full = v0 == kBlock && v1 == kBlock;
+    int v0 = kBlock, v1 = kBlock;
+    bool full = true;
+    if constexpr (!FULL) {
+      const int ip0 = 2 * pp;
+      v0 = ids[ip0] < 0 ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0));
+      // the odd page's keys use the group parameters stored with the even page
+      v1 = (ids[ip0] < 0 || ids[ip0 + 1] < 0) ? 0 : min(kBlock, rq.ctx_len - kBlock * (it.p_lo + ip0 + 1));
+      full = v0 == kBlock && v1 == kBlock;
+    }
     // ---- online softmax over this lane's 8 keys
     float sv[8];
 #pragma unroll
@@ -1591,7 +1623,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       }
     }
   };
-  for (int k = 0; k < mine; ++k) {
+  auto step = [&](int k, auto full_pair) {
     wait_ahead<R::kLoads, STG - 2>(min(STG - 2, mine - 1 - k));
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     if (k + STG - 1 < mine) issue(k + STG - 1, __builtin_amdgcn_readfirstlane(pf0), __builtin_amdgcn_readfirstlane(pf1));
@@ -1599,8 +1631,15 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     const uint8_t* slot = ring + (k % STG) * R::kSlot;
     f32x4 s_acc[2];
     scores(slot, s_acc);
-    consume(k, slot, s_acc);
-  }
+    consume(k, slot, s_acc, full_pair);
+  };
+  // pairs before the first missing or partial page are full; this wave's k-th pair is w + NW k
+  const int nfull = min(it.nctx, max(0, (rq.ctx_len - kBlock * it.p_lo) / kBlock));
+  const int pairs_full = min(nfull, *first_bad) >> 1;
+  const int k_full = min(mine, pairs_full > w ? (pairs_full - w + NW - 1) / NW : 0);
+  int k = 0;
+  for (; k < k_full; ++k) step(k, std::true_type{});
+  for (; k < mine; ++k) step(k, std::false_type{});
 
   // the value bias joins the outputs before any pair that rescales without it
 #pragma unroll
