@@ -856,7 +856,8 @@ template <int D, int NW>
 __device__ __forceinline__ void draft_merge(const AttnArgs& a, const ItemCtx& it, uint8_t* smem,
                                             const f32x4* acc_o, float m_run, float l_run) {
   constexpr int ND = D / 16;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   float* red = reinterpret_cast<float*>(smem);  // [wave][16 rows][D + 4]
   constexpr int RS = D + 4;
 #pragma unroll
@@ -982,7 +983,8 @@ __device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   static_assert(NW * STG * R::kSlot <= R::kRing, "draft rings exceed their LDS");
   constexpr int NS = D / 32;  // k-steps of the score product
   constexpr int ND = D / 16;  // 16-wide d blocks of the output
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const ReqDev& rq = it.rq;
   const int G = a.G;
   const bool row_ok = n < it.rows_total;
@@ -1256,7 +1258,8 @@ __device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) 
   constexpr bool KIVI = BITS != 16;
   constexpr int NS = D / 32;   // k-steps of the score product (16x16x32)
   constexpr int ND = D / 16;   // 16-wide d blocks of the output
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const ReqDev& rq = it.rq;
   const int G = a.G;
   const bool row_ok = n < it.rows_total;
@@ -1434,7 +1437,8 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   constexpr int ND = D / 16;              // 16-wide channel blocks of the output
   constexpr int NGQ = D / 32;             // value channel groups
   constexpr int KW = (D / 4) * BITS / 32; // words of a key row held by one lane (its D/4 channels)
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const ReqDev& rq = it.rq;
   const int G = a.G;
   const bool row_ok = n < it.rows_total;
