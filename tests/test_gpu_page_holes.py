@@ -62,6 +62,7 @@ def test_verify_skips_missing_pages(name, kw, split):
 @pytest.mark.parametrize("name,holes", [
     ("C2", {0: [2, 5, 23], 1: [0, 11]}),          # bf16 drop cache (kept tokens in pages)
     ("C3", {0: [5, 10, 62], 1: [0, 33]}),         # KIVI-2: odd page, even page (pair), the odd last page
+    ("C4", {0: [3, 6, 23], 1: [0, 9]}),           # drop + KIVI-4 (4-bit ring, 24 kept pages)
 ])
 def test_draft_skips_missing_pages(name, holes):
     require_gpu()
