@@ -86,10 +86,6 @@ __device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
-  return __builtin_bit_cast(float, b << 16);
-}
-
 // zero the bf16 lanes t (0..7) of a 16-byte chunk with first + t >= valid
 __device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int first, int valid) {
 #pragma unroll
@@ -1253,46 +1249,6 @@ __device__ __forceinline__ void draft_pair_generic(const AttnArgs& a, const Item
   }
 }
 
-template <int D, int BITS, int NW>
-__device__ void draft_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
-  constexpr bool KIVI = BITS != 16;
-  constexpr int NS = D / 32;   // k-steps of the score product (16x16x32)
-  constexpr int ND = D / 16;   // 16-wide d blocks of the output
-  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
-  const ReqDev& rq = it.rq;
-  const int G = a.G;
-  const bool row_ok = n < it.rows_total;
-  const int tok = row_ok ? n / G : 0;
-  const int qpos = rq.q0 + tok;
-
-  u32x4 qreg[NS];
-  {
-    const uint16_t* qp = a.q + ((((int64_t)rq.slot * a.L + it.l) * a.xmax + rq.q0 + tok) * a.Hq +
-                                it.g * G + (row_ok ? n % G : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qreg[s] = row_ok ? ld16(qp + (KIVI ? draft_chan<D>(kg, s) : 32 * s + 8 * kg)) : u32x4{0, 0, 0, 0};
-    if constexpr (KIVI) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) qreg[s] = bf16x8_to_f16x8(qreg[s]);
-    }
-  }
-
-  f32x4 acc_o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) acc_o[i] = f32x4{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sc = a.scale_log2;
-  const int npairs = (it.npages + 1) >> 1;
-  for (int pp = w; pp < npairs; pp += NW)
-    draft_pair_generic<D, BITS>(a, it, pp, qreg, qpos, sc, acc_o, m_run, l_run);
-
-  // ---- merge the waves' states through LDS
-  l_run = wave_xor_sum(l_run, 16);
-  l_run = wave_xor_sum(l_run, 32);
-  draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
-}
 
 // ------------------------------------------------------------------ draft path, KIVI caches (ring)
 // Whole context page pairs (one 32-token key-quantisation group each) stream through a private
@@ -1661,11 +1617,6 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   l_run = wave_xor_sum(l_run, 32);
   draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
 }
-
-template <int D>
-struct DraftSmem {
-  static constexpr int kBytes = kDWaves * 16 * (D + 4) * 4;  // per-wave softmax states
-};
 
 // Work item -> (request, row group, split, kv head, layer).  Work-groups are dealt round-robin
 // over the 8 XCDs; consecutive items are mapped to one XCD so that items that share K/V (row
