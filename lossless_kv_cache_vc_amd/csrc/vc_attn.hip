@@ -456,6 +456,80 @@ __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>
   }
 }
 
+// Online softmax of tile t (scores s_acc) fused with the score product of tile t + 1 (key
+// stage `stn`), for one wave: the running max moves first (the lazy rescale is a branch), so the
+// exponentials of tile t, the score MFMAs of tile t + 1 and the value MFMAs of tile t sit in one
+// basic block, which the compiler interleaves (a score chain alone in its own block overlapped
+// nothing but the row max).  Returns the scores of tile t + 1.  MASK as in verify_consume.
+template <int D, bool MASK>
+__device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>& vs, const uint8_t* smem,
+                                               int t, int stn, int vst, f32x16 s_acc) {
+  using R = VRing<D>;
+  constexpr int NS = VerifyState<D>::NS;
+  constexpr int ND = VerifyState<D>::ND;
+  const int h = vs.h;
+  VPage p0, p1;
+  if constexpr (MASK) {
+    p0 = vpage_info(it, vs.units, 4 * t + 2 * vs.kh);
+    p1 = vpage_info(it, vs.units, 4 * t + 2 * vs.kh + 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!vkey_visible(r < 8 ? p0 : p1, 8 * h + (r & 7), vs.qpos)) s_acc[r] = -INFINITY;
+  }
+  float mloc = max16(s_acc);
+  mloc = half_swap_max(mloc);
+  const float sc = vs.sc;
+  const float m_new = fmaxf(vs.m_run, mloc * sc);
+  if (__any(m_new > vs.m_run + kLazyRescale)) {
+    const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
+    vs.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) vs.acc_o[i] *= alpha;
+    vs.m_run = m_new;
+  }
+  const float m_use = (vs.m_run == -INFINITY) ? 0.f : vs.m_run;
+
+  // score operands of tile t + 1, then its MFMA chain beside tile t's exponentials
+  const uint8_t* kst = smem + stn * R::kTileK;
+  u32x4 kop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) kop[s] = ld16(kst + vs.koff[s]);
+  f32x16 s_nxt = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop[s]), as_bf(vs.qreg[s]), s_nxt, 0, 0, 0);
+  float e[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[r], sc, -m_use));
+
+  // value operands and the value product of tile t
+  const uint8_t* vbase = smem + vst * R::kTileK + vs.voff;
+  u32x4 vop[2][ND];
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      vop[pj][db] = ld16(vbase + pj * R::kPage + db * 1024);
+      if constexpr (MASK) vop[pj][db] = mask_tokens(vop[pj][db], 8 * h, (pj ? p1 : p0).valid);
+    }
+  uint32_t pb[8];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) pb[r >> 1] = pack_bf16(e[r], e[r + 1]);
+#pragma unroll
+  for (int pj = 0; pj < 2; ++pj) {
+    const u32x4 bv = {pb[4 * pj], pb[4 * pj + 1], pb[4 * pj + 2], pb[4 * pj + 3]};
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      vs.acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop[pj][db]), as_bf(bv), vs.acc_o[db], 0, 0, 0);
+  }
+  float ls[4] = {e[0], e[1], e[2], e[3]};
+#pragma unroll
+  for (int r = 4; r < 16; ++r) ls[r & 3] += e[r];
+  vs.l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+  return s_nxt;
+}
+
 // One tile: wait for K(t + 1) (key waves) / V(t) (value waves), refill the dead stages (K(t + 4)
 // into key stage t % 4, V(t + 3) into value stage (t - 1) % 4), score tile t + 1 into s_nxt (the
 // last tile scores a stale stage, unused) and consume tile t.  STC >= 0: t % 4 == STC known at
@@ -484,8 +558,7 @@ __device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it
   }
   vs.vst = vst == kVVStages - 1 ? 0 : vst + 1;
   if (!vs.wave_on) return;
-  s_nxt = verify_scores<D>(smem, (st + 1) & (kVStages - 1), vs);
-  verify_consume<D, MASK>(it, vs, smem, t, vst, s_cur);
+  s_nxt = verify_fused<D, MASK>(it, vs, smem, t, (st + 1) & (kVStages - 1), vst, s_cur);
 }
 
 // Byte offset inside a K or V page of this lane's part of ring load i.  The LDS side of
@@ -1711,45 +1784,57 @@ __global__ __launch_bounds__(kVThreads) void mixed_kernel(const AttnArgs a) {
   else draft_dispatch<D, kVWaves>(a, it, smem);
 }
 
-// Combine split partials: one work-group per (request, layer, kv head) with nsplit > 1.
+// Combine split partials with log-sum-exp weights.  A row's D outputs are spread over D / 4
+// lanes (4 channels each), so a work-group of 256 threads merges 256 / (D / 4) rows; rows are
+// numbered over the (layer, kv head) units of the split requests in request order.  One pass
+// over the splits: the running maximum moves when a split's is larger (the sum and the output
+// are rescaled then).
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
-  int b = blockIdx.x;
+  constexpr int LPR = D / 4;
+  constexpr int RPB = 256 / LPR;
+  int64_t rg = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int cq = threadIdx.x % LPR;
   int r = -1;
   for (int i = 0; i < a.nreq; ++i) {
     if (a.reqs[i].nsplit <= 1) continue;
-    const int cnt = a.L * a.Hkv;
-    if (b < cnt) {
+    const int64_t cnt = (int64_t)a.L * a.Hkv * a.reqs[i].rows * a.G;
+    if (rg < cnt) {
       r = i;
       break;
     }
-    b -= cnt;
+    rg -= cnt;
   }
   if (r < 0) return;
   const ReqDev& rq = a.reqs[r];
-  const int g = b % a.Hkv, l = b / a.Hkv;
   const int rows_total = rq.rows * a.G;
-  constexpr int NQ = D / 4;
-  for (int task = threadIdx.x; task < rows_total * NQ; task += 256) {
-    const int row = task / NQ, cq = task % NQ;
-    const float* base = a.part + rq.part_base +
-                        ((((int64_t)l * a.Hkv + g) * rq.nsplit) * rows_total + row) * (D + 4);
-    const int64_t sstride = (int64_t)rows_total * (D + 4);
-    float M = -INFINITY;
-    for (int s = 0; s < rq.nsplit; ++s) M = fmaxf(M, base[s * sstride + D]);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-    for (int s = 0; s < rq.nsplit; ++s) {
-      const float ms = base[s * sstride + D];
-      const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      lsum += f * base[s * sstride + D + 1];
-      o += f * *reinterpret_cast<const f32x4*>(base + s * sstride + 4 * cq);
+  const int64_t unit = rg / rows_total;  // l * Hkv + g
+  const int row = (int)(rg % rows_total);
+  const int g = (int)(unit % a.Hkv), l = (int)(unit / a.Hkv);
+  const float* base = a.part + rq.part_base + ((unit * rq.nsplit) * rows_total + row) * (D + 4);
+  const int64_t sstride = (int64_t)rows_total * (D + 4);
+  float M = -INFINITY, lsum = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < rq.nsplit; ++s) {
+    const float* p = base + s * sstride;
+    const float ms = p[D], ls = p[D + 1];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(p + 4 * cq);
+    if (ms == -INFINITY) continue;  // a split with no visible key
+    if (ms > M) {
+      const float c = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - ms);
+      o *= c;
+      lsum *= c;
+      M = ms;
     }
-    o *= lsum > 0.f ? 1.f / lsum : 0.f;
-    const int tok = row / a.G, jh = row % a.G;
-    float* dst = a.out + ((((int64_t)rq.slot * a.L + l) * a.xmax + rq.q0 + tok) * a.Hq + g * a.G + jh) * D;
-    *reinterpret_cast<f32x4*>(dst + 4 * cq) = o;
+    const float f = __builtin_amdgcn_exp2f(ms - M);
+    lsum += f * ls;
+    o += f * os;
   }
+  o *= lsum > 0.f ? 1.f / lsum : 0.f;
+  const int tok = row / a.G, jh = row % a.G;
+  float* dst = a.out + ((((int64_t)rq.slot * a.L + l) * a.xmax + rq.q0 + tok) * a.Hq + g * a.G + jh) * D;
+  *reinterpret_cast<f32x4*>(dst + 4 * cq) = o;
 }
 
 }  // namespace
@@ -1783,11 +1868,13 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
   int rc = hip_check(hipGetLastError(), "attention launch");
   if (rc) return rc;
   if (plan.any_split) {
-    int nmerge = 0;
+    int64_t nmerge = 0;
     for (int i = 0; i < args.nreq; ++i)
-      if (args.reqs[i].nsplit > 1) nmerge += args.L * args.Hkv;
-    if (head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(nmerge), dim3(256), 0, stream, args);
-    else hipLaunchKernelGGL(merge_kernel<64>, dim3(nmerge), dim3(256), 0, stream, args);
+      if (args.reqs[i].nsplit > 1) nmerge += (int64_t)args.L * args.Hkv * args.reqs[i].rows * args.G;
+    const int rpb = 256 / (head_dim / 4);  // rows per merge work-group
+    const dim3 mgrid((unsigned)((nmerge + rpb - 1) / rpb));
+    if (head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, args);
+    else hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, args);
     rc = hip_check(hipGetLastError(), "merge launch");
   }
   return rc;
