@@ -1,0 +1,101 @@
+"""Properties the method fixes, checked on the GPU path against the oracle (run on an MI355X: -m gpu).
+
+* Lossless drafting (VeriCache review, §Draft–Verify Pipeline: the drafter is lossy only through
+  its key set and values): a drafting cache that keeps every context token gives draft step i
+  the key set and values of verify row i.  The draft and verify kernels then agree to their own
+  rounding, their argmax tokens agree except at near-ties the oracle flags, and every drafted
+  token is accepted (a = x).
+* Verify with one drafted row is a decode step: it equals draft step 0 over the same keep-all
+  cache.
+* A request with no context tokens attends only to its drafted block (rows 0..i), in both passes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_close, require_gpu, tight_tol, tokens_match
+from oracle import workload as ow
+from vcsynth import configs as C
+
+pytestmark = pytest.mark.gpu
+
+
+def keep_all(cfg):
+    for r in cfg.reqs:
+        r.comp, r.recent, r.top = C.COMP_DROP, r.ctx_len, 0
+    return cfg
+
+
+def run_round(cfg):
+    require_gpu()
+    from lossless_kv_cache_vc_amd.harness import Workload
+    wl = Workload(cfg)
+    for i in range(max(r.x for r in cfg.reqs)):
+        wl.run_draft(i)
+    wl.run_verify()
+    wl.logits_and_accept()
+    torch.cuda.synchronize()
+    return wl
+
+
+def outputs(wl, cfg):
+    """(draft, verify) outputs as float64 [B][L][xmax][Hq][d]."""
+    return (wl.out_d.cpu().numpy().astype(np.float64), wl.out_v.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("name,kw", [("C1", dict(n=1000)), ("C2", dict(L=2, B=2, n=1000, x=8))])
+def test_keep_all_draft_equals_verify_and_accepts_all(name, kw):
+    cfg = keep_all(C.scaled(C.get(name), **kw))
+    print(f"keep-all {cfg.name} {kw}", flush=True)
+    wl = run_round(cfg)
+    od, ov = outputs(wl, cfg)
+    tok_d, tok_v = wl.tok_d.cpu().numpy(), wl.tok_v.cpu().numpy()
+    alen, nxt = wl.acc_len.cpu().numpy(), wl.next_tok.cpu().numpy()
+    worst = 0.0
+    for r, req in enumerate(cfg.reqs):
+        x = req.x
+        tol = tight_tol(req.ctx_len)
+        for l in range(cfg.L):
+            inst = r * cfg.L + l
+            # the two kernels compute the same attention: each is within the gate of the exact
+            # value, so they are within twice the gate of each other
+            worst = max(worst, assert_close(od[r, l, :x], ov[r, l, :x], 2 * tol, f"draft-vs-verify r={r} l={l}"))
+            res = ow.round_instance(cfg, r, l)
+            assert res.accept_len == x and res.next_tok == -1  # the oracle: lossless, all accepted
+            assert_close(od[r, l, :x], res.draft_o, tol, f"draft r={r} l={l}")
+            assert_close(ov[r, l, :x], res.verify_o, tol, f"verify r={r} l={l}")
+            assert not tokens_match(tok_d[inst, :x], res.draft_tok, res.draft_gap, res.draft_logits)
+            assert not tokens_match(tok_v[inst, :x], res.verify_tok, res.verify_gap, res.verify_logits)
+            if not res.flagged:
+                assert np.array_equal(tok_d[inst, :x], tok_v[inst, :x])
+                assert alen[inst] == x and nxt[inst] == -1
+    print(f"{cfg.name}: draft-vs-verify max-abs {worst:.3e}")
+
+
+def test_verify_of_one_row_is_a_decode_step():
+    cfg = keep_all(C.scaled(C.get("C2"), L=2, B=2, n=777, x=1))
+    print(f"x=1 {cfg.name}", flush=True)
+    wl = run_round(cfg)
+    od, ov = outputs(wl, cfg)
+    for r, req in enumerate(cfg.reqs):
+        for l in range(cfg.L):
+            assert_close(ov[r, l, :1], od[r, l, :1], 2 * tight_tol(req.ctx_len), f"x=1 r={r} l={l}")
+            res = ow.round_instance(cfg, r, l)
+            assert_close(ov[r, l, :1], res.verify_o, tight_tol(req.ctx_len), f"x=1 verify r={r} l={l}")
+
+
+def test_request_without_context_sees_only_its_block():
+    cfg = C.scaled(C.get("C2"), L=1, B=3, n=1000, x=8)
+    for r, n in zip(cfg.reqs, (1000, 0, 37)):
+        r.ctx_len, r.recent, r.top = n, min(128, n), n // 4
+    print(f"context lengths 1000, 0, 37 {cfg.name}", flush=True)
+    wl = run_round(cfg)
+    od, ov = outputs(wl, cfg)
+    for r, req in enumerate(cfg.reqs):
+        x, tol = req.x, tight_tol(max(1, req.ctx_len))
+        res = ow.round_instance(cfg, r, 0)
+        assert_close(ov[r, 0, :x], res.verify_o, tol, f"verify n={req.ctx_len}")
+        assert_close(od[r, 0, :x], res.draft_o, tol, f"draft n={req.ctx_len}")
+        if req.ctx_len == 0:
+            # nothing but the drafted block, in both passes: the same keys, so the same outputs
+            assert_close(od[r, 0, :x], ov[r, 0, :x], 2 * tol, "n=0 draft-vs-verify")
