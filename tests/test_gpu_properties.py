@@ -8,6 +8,8 @@
 * Verify with one drafted row is a decode step: it equals draft step 0 over the same keep-all
   cache.
 * A request with no context tokens attends only to its drafted block (rows 0..i), in both passes.
+* KIVI quantisation that is exact on its inputs (context values on the quantiser's lattice) makes
+  the 2- and 4-bit drafters lossless too: the KIVI draft kernel matches the verify kernel.
 """
 import numpy as np
 import pytest
@@ -99,3 +101,69 @@ def test_request_without_context_sees_only_its_block():
         if req.ctx_len == 0:
             # nothing but the drafted block, in both passes: the same keys, so the same outputs
             assert_close(od[r, 0, :x], ov[r, 0, :x], 2 * tol, "n=0 draft-vs-verify")
+
+
+def lattice_context(n, d, hkv, bits, seed):
+    """Context K or V [1][hkv][n][d] on the KIVI lattice z + s*code with s = 4 / (Lq + 1) and
+    z = -Lq*s/2 (2-bit: -1.5, -0.5, 0.5, 1.5; 4-bit: -1.875 .. 1.875 in steps of 1/4; exact in
+    bf16 and fp16).  Code 0 sits where (token - channel) % 32 == 0 and Lq where it is 1, so every
+    32-token key group of a channel and every 32-channel value group of a token holds both ends:
+    its min-max quantisation recovers s, z and the codes exactly.  Other codes are seeded draws."""
+    lq = (1 << bits) - 1
+    gen = torch.Generator().manual_seed(seed)
+    codes = torch.randint(0, lq + 1, (1, hkv, n, d), generator=gen)
+    diff = (torch.arange(n).view(n, 1) - torch.arange(d).view(1, d)) % 32
+    codes[:, :, diff == 0] = 0
+    codes[:, :, diff == 1] = lq
+    step = 4.0 / (lq + 1)
+    return (-lq * step / 2 + step * codes.double()).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("comp,bits,base", [(C.COMP_KIVI2, 2, "C3"), (C.COMP_DROP_KIVI4, 4, "C4")])
+def test_lattice_kivi_draft_equals_verify_and_accepts_all(comp, bits, base):
+    """Quantisation that is exact on its inputs makes the KIVI drafter lossless: the KIVI draft
+    kernel and the verify kernel see the same keys and values, so they agree to their rounding and
+    every drafted token is accepted.  Rows whose verify top-2 logit gap is under 1e-3 are near-ties
+    (flagged, as in the oracle comparisons): tokens are compared on the other rows, and the accept
+    length must reach the first near-tie row."""
+    require_gpu()
+    from lossless_kv_cache_vc_amd import vc
+    from lossless_kv_cache_vc_amd.harness import Workload
+    cfg = C.scaled(C.get(base), L=2, B=2, n=1024, x=8)
+    for r in cfg.reqs:
+        r.comp, r.recent, r.top = comp, r.ctx_len, 0   # drop + KIVI-4: keep every token
+    print(f"lattice KIVI-{bits} {cfg.name}", flush=True)
+    wl = Workload(cfg, build_compressed=False)
+    for r, n in enumerate(wl.lens):
+        row = wl._row(wl.full, r)
+        for l in range(cfg.L):
+            for which in (0, 1):
+                src = lattice_context(n, cfg.d, cfg.Hkv, bits, seed=1000 * r + 10 * l + which).to(wl.dev)
+                vc.pack_bf16(wl.shape, [n], l, src, n, row, which)
+    wl._build_compressed(False)
+    wl.workspace = wl._workspace()
+    for i in range(max(r.x for r in cfg.reqs)):
+        wl.run_draft(i)
+    wl.run_verify()
+    wl.logits_and_accept()
+    torch.cuda.synchronize()
+    od, ov = outputs(wl, cfg)
+    tok_d, tok_v = wl.tok_d.cpu().numpy(), wl.tok_v.cpu().numpy()
+    alen = wl.acc_len.cpu().numpy()
+    zv = wl.z_v.cpu().numpy().reshape(cfg.B * cfg.L, wl.xmax, -1)
+    worst, full = 0.0, 0
+    for r, req in enumerate(cfg.reqs):
+        x = req.x
+        for l in range(cfg.L):
+            inst = r * cfg.L + l
+            worst = max(worst, assert_close(od[r, l, :x], ov[r, l, :x], 2 * tight_tol(req.ctx_len, kivi=True),
+                                            f"KIVI-{bits} draft-vs-verify r={r} l={l}"))
+            top2 = np.sort(zv[inst, :x], axis=1)[:, -2:]
+            clear = (top2[:, 1] - top2[:, 0]) >= 1e-3
+            assert np.array_equal(tok_d[inst, :x][clear], tok_v[inst, :x][clear])
+            # accepted at least up to the first near-tie row (all x when there is none)
+            first = int(np.argmin(clear)) if not clear.all() else x
+            assert alen[inst] >= first
+            full += first == x
+    print(f"KIVI-{bits}: draft-vs-verify max-abs {worst:.3e}; {full} of {cfg.B * cfg.L} instances "
+          f"without a near-tie row, all accepted")
