@@ -210,7 +210,8 @@ int vc_accept_sampled(int n_inst, int max_x, int max_xv, int vocab, float temper
 
 /*
  * LM-head stand-in used to turn attention outputs into logits: z[r][v] = sum_w o[r][w] * W_u[w][v]
- * (fp32 accumulate).  o fp32 [rows][width] with row stride ld_o floats; w_u bf16 [width][vocab];
+ * (bf16 MFMA, fp32 accumulate; each element of o enters as two bf16 parts whose sum is within
+ * 2^-18 of it, so z carries fp32 accumulation error only).  o fp32 [rows][width] with row stride ld_o floats; w_u bf16 [width][vocab];
  * z fp32 [rows][vocab].  VeriCache review, §Draft–Verify Pipeline: argmax over the logits of
  * each position.
  */

@@ -76,54 +76,121 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(int max_x, int max_
     vtok[(int64_t)inst * max_xv + i] = i < nxv ? tv[i] : -1;
 }
 
-// z = o * W_u, fp32 accumulate.  64x64 output tile per work-group, 4x4 per thread, K steps of 32.
-constexpr int kTM = 64, kTN = 64, kTK = 32;
+// z = o * W_u on bf16 MFMA with fp32 accumulation.  Each fp32 element x of o is split into
+// bf16 hi = RNE(x) and lo = RNE(x - hi) (x - hi is exact in fp32, so |x - hi - lo| <= 2^-18 |x|);
+// W_u is bf16, so hi * w and lo * w are exact in fp32 and z carries only fp32 accumulation error.
+// A work-group of 4 waves computes a 128 x 128 tile of z, each wave 64 x 64 (2 x 2 blocks of
+// 32 x 32, v_mfma_f32_32x32x16_bf16), over K steps of 32 staged in LDS: o as hi and lo [m][k],
+// W_u transposed to [n][k], so every MFMA operand is one 16-byte LDS read; rows are padded to 40
+// bf16 (80 bytes) so the reads of a 32-lane half fall on distinct banks.  VEC: o rows, W_u rows
+// and the bases allow 16-byte global loads.
+constexpr int kLM = 128, kLN = 128, kLK = 32, kLPad = 40;
 
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void logits_kernel(int rows, int width, int vocab, const float* o,
                                                      int64_t ld_o, const uint16_t* wu, float* z) {
-  __shared__ float sa[kTK][kTM + 4];  // o tile, transposed: [k][m]
-  __shared__ float sb[kTK][kTN + 4];  // W tile: [k][n]
-  const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < width; k0 += kTK) {
-    for (int e = threadIdx.x; e < kTM * kTK; e += 256) {
-      const int mm = e / kTK, kk = e % kTK;
-      const int gm = m0 + mm, gk = k0 + kk;
-      sa[kk][mm] = (gm < rows && gk < width) ? o[(int64_t)gm * ld_o + gk] : 0.f;
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[kLM * kLPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lo[kLM * kLPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kLN * kLPad];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m0 = blockIdx.y * kLM, n0 = blockIdx.x * kLN;
+  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;  // this wave's 64 x 64 part of the tile
+  const int r32 = lane & 31, kh = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  for (int k0 = 0; k0 < width; k0 += kLK) {
+    // o: 128 rows x 32 k, 4 consecutive k per thread and step
+#pragma unroll
+    for (int e = tid; e < kLM * kLK / 4; e += 256) {
+      const int mm = e / (kLK / 4), kq = (e % (kLK / 4)) * 4;
+      const int gm = m0 + mm, gk = k0 + kq;
+      float v[4];
+      if constexpr (VEC) {  // width % 4 == 0: the 4 elements are all inside or all outside
+        const f32x4 t = (gm < rows && gk < width) ? *reinterpret_cast<const f32x4*>(o + (int64_t)gm * ld_o + gk)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = t[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (gm < rows && gk + j < width) ? o[(int64_t)gm * ld_o + gk + j] : 0.f;
+      }
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const uint16_t h0 = bf16_bits(v[j]), h1 = bf16_bits(v[j + 1]);
+        const float r0 = v[j] - __builtin_bit_cast(float, (uint32_t)h0 << 16);
+        const float r1 = v[j + 1] - __builtin_bit_cast(float, (uint32_t)h1 << 16);
+        hi[j >> 1] = h0 | ((uint32_t)h1 << 16);
+        lo[j >> 1] = bf16_bits(r0) | ((uint32_t)bf16_bits(r1) << 16);
+      }
+      *reinterpret_cast<u32x2*>(s_hi + mm * kLPad + kq) = u32x2{hi[0], hi[1]};
+      *reinterpret_cast<u32x2*>(s_lo + mm * kLPad + kq) = u32x2{lo[0], lo[1]};
     }
-    for (int e = threadIdx.x; e < kTK * kTN; e += 256) {
-      const int kk = e / kTN, nn = e % kTN;
-      const int gk = k0 + kk, gn = n0 + nn;
-      sb[kk][nn] = (gk < width && gn < vocab)
-                       ? __builtin_bit_cast(float, (uint32_t)wu[(int64_t)gk * vocab + gn] << 16)
-                       : 0.f;
+    // W_u: 32 k x 128 n, 8 consecutive n per thread and step, stored transposed ([n][k]);
+    // consecutive threads take consecutive k, so the 2-byte LDS writes spread over the banks
+#pragma unroll
+    for (int e = tid; e < kLK * kLN / 8; e += 256) {
+      const int kk = e % kLK, nq = (e / kLK) * 8;
+      const int gk = k0 + kk, gn = n0 + nq;
+      uint16_t v[8];
+      if constexpr (VEC) {  // vocab % 8 == 0
+        const u32x4 t = (gk < width && gn < vocab) ? *reinterpret_cast<const u32x4*>(wu + (int64_t)gk * vocab + gn)
+                                                   : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = (uint16_t)(t[j] & 0xFFFFu);
+          v[2 * j + 1] = (uint16_t)(t[j] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (gk < width && gn + j < vocab) ? wu[(int64_t)gk * vocab + gn + j] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_w[(nq + j) * kLPad + kk] = v[j];
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kTK; ++kk) {
-      float av[4], bv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = sa[kk][ty * 4 + i];
+    for (int ks = 0; ks < kLK / 16; ++ks) {
+      const int kc = ks * 16 + kh * 8;  // lane's 8 k of this 16-k step
+      u32x4 ah[2], al[2], bw[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = sb[kk][tx * 4 + j];
+      for (int i = 0; i < 2; ++i) {
+        ah[i] = *reinterpret_cast<const u32x4*>(s_hi + (wm + 32 * i + r32) * kLPad + kc);
+        al[i] = *reinterpret_cast<const u32x4*>(s_lo + (wm + 32 * i + r32) * kLPad + kc);
+        bw[i] = *reinterpret_cast<const u32x4*>(s_w + (wn + 32 * i + r32) * kLPad + kc);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
+                                                              __builtin_bit_cast(bf16x8, bw[j]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al[i]),
+                                                              __builtin_bit_cast(bf16x8, bw[j]), acc[i][j], 0, 0, 0);
+        }
     }
     __syncthreads();
   }
+  // accumulator r of a 32 x 32 block: row 8 (r / 4) + 4 kh + r % 4, column r32
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + ty * 4 + i;
-    if (gm >= rows) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tx * 4 + j;
-      if (gn < vocab) z[(int64_t)gm * vocab + gn] = acc[i][j];
+    for (int j = 0; j < 2; ++j) {
+      const int gn = n0 + wn + 32 * j + r32;
+      if (gn >= vocab) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (gm < rows) z[(int64_t)gm * vocab + gn] = acc[i][j][r];
+      }
     }
-  }
 }
 
 }  // namespace
@@ -158,9 +225,17 @@ int vc_logits(int rows, int width, int vocab, const float* o, int64_t ld_o, cons
   if (rows < 0 || width < 1 || vocab < 1 || ld_o < width) return fail(VC_EINVAL, "bad logits shape");
   if (rows == 0) return VC_OK;
   if (!o || !w_u || !z) return fail(VC_EINVAL, "NULL argument");
-  dim3 grid((vocab + kTN - 1) / kTN, (rows + kTM - 1) / kTM);
-  hipLaunchKernelGGL(logits_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), rows, width,
-                     vocab, o, ld_o, static_cast<const uint16_t*>(w_u), z);
+  if ((rows + kLM - 1) / kLM > 65535) return fail(VC_EINVAL, "too many logits rows");
+  const dim3 grid((vocab + kLN - 1) / kLN, (rows + kLM - 1) / kLM);
+  const bool vec = ld_o % 4 == 0 && width % 4 == 0 && vocab % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(o) % 16 == 0 && reinterpret_cast<uintptr_t>(w_u) % 16 == 0;
+  const uint16_t* wu = static_cast<const uint16_t*>(w_u);
+  if (vec)
+    hipLaunchKernelGGL(logits_kernel<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), rows, width,
+                       vocab, o, ld_o, wu, z);
+  else
+    hipLaunchKernelGGL(logits_kernel<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), rows, width,
+                       vocab, o, ld_o, wu, z);
   return hip_check(hipGetLastError(), "logits launch");
 }
 
