@@ -11,32 +11,54 @@ namespace vc {
 
 namespace {
 
-constexpr int kAccThreads = 256;
+constexpr int kAccThreads = 1024;  // 16 waves per instance: its draft and verify rows in parallel
 
-// argmax of one row by one wave: ties go to the lowest index
+// fold (z, v) into a lane's running (best, index): larger value wins, ties to the lower index
+__device__ __forceinline__ void arg_fold(float z, int v, float& best, int& bi) {
+  if (z > best || (z == best && v < bi)) {
+    best = z;
+    bi = v;
+  }
+}
+
+// argmax of one row by one wave: ties go to the lowest index.  VEC: the row is 16-byte aligned
+// and vocab % 4 == 0, so each lane reads 4 consecutive logits per load, 4 loads in flight.
+template <bool VEC>
 __device__ int wave_argmax(const float* row, int vocab) {
   const int lane = threadIdx.x & 63;
   float best = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int v = lane; v < vocab; v += 64) {
-    const float z = row[v];
-    if (z > best || (z == best && v < bi)) {
-      best = z;
-      bi = v;
+  if constexpr (VEC) {
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
+    const int n4 = vocab >> 2;
+    int i = lane;
+    for (; i + 192 < n4; i += 256) {
+      f32x4 c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = r4[i + 64 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) arg_fold(c[u][e], 4 * (i + 64 * u) + e, best, bi);
     }
+    for (; i < n4; i += 64) {
+      const f32x4 c = r4[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) arg_fold(c[e], 4 * i + e, best, bi);
+    }
+  } else {
+    for (int v = lane; v < vocab; v += 64) arg_fold(row[v], v, best, bi);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ob = __shfl_xor(best, o);
     const int oi = __shfl_xor(bi, o);
-    if (ob > best || (ob == best && oi < bi)) {
-      best = ob;
-      bi = oi;
-    }
+    arg_fold(ob, oi, best, bi);
   }
   return bi == 0x7FFFFFFF ? 0 : bi;
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kAccThreads) void accept_kernel(int max_x, int max_xv, int vocab, const int32_t* x,
                                                              const int32_t* xv, const float* dl,
                                                              const float* vl, int32_t* dtok,
@@ -51,11 +73,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(int max_x, int max_
   // draft rows then verify rows, one row per wave at a time
   for (int rr = w; rr < nx + nxv; rr += nw) {
     if (rr < nx) {
-      const int t = wave_argmax(dl + ((int64_t)inst * max_x + rr) * vocab, vocab);
+      const int t = wave_argmax<VEC>(dl + ((int64_t)inst * max_x + rr) * vocab, vocab);
       if (lane == 0) td[rr] = t;
     } else {
       const int j = rr - nx;
-      const int t = wave_argmax(vl + ((int64_t)inst * max_xv + j) * vocab, vocab);
+      const int t = wave_argmax<VEC>(vl + ((int64_t)inst * max_xv + j) * vocab, vocab);
       if (lane == 0) tv[j] = t;
     }
   }
@@ -213,9 +235,16 @@ int vc_accept(int n_inst, int max_x, int max_xv, int vocab, const int32_t* x, co
   if (!x || !xv || !draft_logits || !verify_logits || !draft_tok || !verify_tok || !accept_len ||
       !next_tok)
     return fail(VC_EINVAL, "NULL argument");
-  hipLaunchKernelGGL(accept_kernel, dim3(n_inst), dim3(kAccThreads), 0, static_cast<hipStream_t>(stream),
-                     max_x, max_xv, vocab, x, xv, draft_logits, verify_logits, draft_tok, verify_tok, accept_len,
-                     next_tok);
+  const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(verify_logits) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(accept_kernel<true>, dim3(n_inst), dim3(kAccThreads), 0, static_cast<hipStream_t>(stream),
+                       max_x, max_xv, vocab, x, xv, draft_logits, verify_logits, draft_tok, verify_tok, accept_len,
+                       next_tok);
+  else
+    hipLaunchKernelGGL(accept_kernel<false>, dim3(n_inst), dim3(kAccThreads), 0, static_cast<hipStream_t>(stream),
+                       max_x, max_xv, vocab, x, xv, draft_logits, verify_logits, draft_tok, verify_tok, accept_len,
+                       next_tok);
   return hip_check(hipGetLastError(), "accept launch");
 }
 

@@ -1,4 +1,5 @@
-"""The LM-head stand-in (vc_logits) against the oracle's fp64 logits (run on an MI355X: -m gpu).
+"""The LM-head stand-in (vc_logits) and the greedy accept (vc_accept) against the oracle (run on an
+MI355X: -m gpu).
 
 z = o * W_u with o fp32 and W_u bf16.  The kernel splits each element of o into two bf16 parts
 and accumulates both products in fp32, so z differs from the exact product by the split's
@@ -43,3 +44,45 @@ def test_logits_match_the_oracle(rows, width, ld_o, vocab):
     assert np.all(np.isfinite(got))
     assert np.all(err <= bound), f"max error {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
     print(f"max abs error {err.max():.3e} (bound at that element {bound.flat[err.argmax()]:.3e})")
+
+
+@pytest.mark.parametrize("vocab", [4096, 1001, 37])
+def test_greedy_accept_matches_the_oracle(vocab):
+    """vc_accept on random logits with planted exact ties (the lowest index must win) and planted
+    agreement, for the 16-byte-load path (vocab % 4 == 0) and the scalar one; block lengths 1..64,
+    half of them with a bonus verifier row (xv = x + 1).  Tokens, accept lengths and next tokens
+    must equal the oracle's exactly."""
+    require_gpu()
+    from lossless_kv_cache_vc_amd import vc
+    print(f"greedy accept vocab={vocab}", flush=True)
+    rng = np.random.default_rng(vocab)
+    n_inst, max_x = 48, 64
+    max_xv = max_x + 1
+    x = rng.integers(1, max_x + 1, n_inst).astype(np.int32)
+    xv = (x + (np.arange(n_inst) % 2)).astype(np.int32)
+    zd = rng.standard_normal((n_inst, max_x, vocab)).astype(np.float32)
+    zv = rng.standard_normal((n_inst, max_xv, vocab)).astype(np.float32)
+    for i in range(n_inst):
+        agree = rng.integers(0, x[i] + 1)  # rows before `agree` share their argmax
+        for j in range(x[i]):
+            t = rng.integers(0, vocab)
+            if j < agree:
+                zd[i, j, t] = zv[i, j, t] = 10.0
+            if j % 3 == 0:  # an exact tie: the lower index must win
+                u = rng.integers(0, vocab)
+                zd[i, j, u] = zd[i, j].max()
+                zv[i, j, u] = zv[i, j].max()
+    to = lambda a: torch.from_numpy(a).cuda()
+    dt = torch.empty((n_inst, max_x), dtype=torch.int32, device="cuda")
+    vt = torch.empty((n_inst, max_xv), dtype=torch.int32, device="cuda")
+    al = torch.empty(n_inst, dtype=torch.int32, device="cuda")
+    nt = torch.empty(n_inst, dtype=torch.int32, device="cuda")
+    vc.accept(n_inst, max_x, max_xv, vocab, to(x), to(xv), to(zd), to(zv), dt, vt, al, nt)
+    torch.cuda.synchronize()
+    dt, vt, al, nt = dt.cpu().numpy(), vt.cpu().numpy(), al.cpu().numpy(), nt.cpu().numpy()
+    for i in range(n_inst):
+        td, _ = oacc.argmax_gap(zd[i, :x[i]].astype(np.float64))
+        tv, _ = oacc.argmax_gap(zv[i, :xv[i]].astype(np.float64))
+        assert np.array_equal(dt[i, :x[i]], td) and np.all(dt[i, x[i]:] == -1)
+        assert np.array_equal(vt[i, :xv[i]], tv) and np.all(vt[i, xv[i]:] == -1)
+        assert (al[i], nt[i]) == oacc.accept(td, tv)
