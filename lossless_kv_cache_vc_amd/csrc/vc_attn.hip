@@ -825,9 +825,10 @@ __device__ __forceinline__ f32x16 wide_scores(const uint8_t* smem, int st, uint3
 
 // One tile: wait for tile t, refill the stage freed by tile t - 1 with tile t + 3, then both
 // key halves of tile t, one after the other.  STC >= 0: t % 4 == STC known at compile time.
-template <int D, int STC, bool MASK>
+template <int D, int STC, bool MASK, bool SPLIT>
 __device__ __forceinline__ void wide_step(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs,
-                                          WideLoads& ld, uint8_t* smem, int t, uint32_t kx, uint32_t voff0) {
+                                          WideLoads& ld, uint8_t* smem, int t, uint32_t kx, uint32_t voff0,
+                                          int kh_only) {
   const int st = STC >= 0 ? STC : (t & (kWStages - 1));
   const int ntiles = vs.ntiles;
   wide_wait<D>(ld.nslot, min(2, ntiles - 1 - t));
@@ -841,23 +842,52 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const ItemCtx& it, 
   ld.pf1 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s1 & 3));
   if (!vs.wave_on) return;
   asm volatile("" : "+v"(kx));  // the 8 operand offsets kx ^ 32 s are derived here, not held
-  vs.kh = 0;
-  vs.voff = voff0;
-  verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 0>(smem, st, kx, vs.qreg));
-  vs.kh = 1;
-  vs.voff = voff0 + 2 * WRing<D>::kPage;
-  verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 1>(smem, st, kx, vs.qreg));
+  if constexpr (SPLIT) {  // one key half (kh_only) of a shared row block
+    vs.kh = kh_only;
+    vs.voff = voff0 + 2 * WRing<D>::kPage * kh_only;
+    verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 0>(smem + kh_only * 32 * (2 * D), st, kx, vs.qreg));
+  } else {
+    vs.kh = 0;
+    vs.voff = voff0;
+    verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 0>(smem, st, kx, vs.qreg));
+    vs.kh = 1;
+    vs.voff = voff0 + 2 * WRing<D>::kPage;
+    verify_consume<D, MASK>(it, vs, smem, t, st, wide_scores<D, 1>(smem, st, kx, vs.qreg));
+  }
+}
+
+// The tile loop of a wide verify wave: full tiles four at a time with compile-time ring stages,
+// then the rest, then the masked tiles.  SPLIT: the wave takes one key half of every tile.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void wide_loop(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs, WideLoads& ld,
+                                          uint8_t* smem, uint32_t kx, uint32_t voff0, int kh_only) {
+  const int ntiles = vs.ntiles;
+  int t = 0;
+  for (; t + 3 < vs.t_full; t += 4) {
+    wide_step<D, 0, false, SPLIT>(a, it, vs, ld, smem, t, kx, voff0, kh_only);
+    wide_step<D, 1, false, SPLIT>(a, it, vs, ld, smem, t + 1, kx, voff0, kh_only);
+    wide_step<D, 2, false, SPLIT>(a, it, vs, ld, smem, t + 2, kx, voff0, kh_only);
+    wide_step<D, 3, false, SPLIT>(a, it, vs, ld, smem, t + 3, kx, voff0, kh_only);
+  }
+  for (; t < vs.t_full; ++t) wide_step<D, -1, false, SPLIT>(a, it, vs, ld, smem, t, kx, voff0, kh_only);
+  for (; t < ntiles; ++t) wide_step<D, -1, true, SPLIT>(a, it, vs, ld, smem, t, kx, voff0, kh_only);
 }
 
 template <int D>
 __device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
   using R = WRing<D>;
   using VS = VerifyState<D>;
-  const int nw = a.vwaves;
+  const int nrb = a.vwaves;  // 32-row blocks per item
+  int nfull;
+  const int nw = wide_waves(nrb, &nfull);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int rows0 = rg * 32 * nw + 32 * w;  // first row of this wave
+  // a whole row block (both key halves of every tile), or one key half of a shared block
+  const bool split = w >= nfull;
+  const int rb = split ? nfull + ((w - nfull) >> 1) : w;
+  const int kh_only = split ? ((w - nfull) & 1) : -1;
+  const int rows0 = rg * 32 * nrb + 32 * rb;  // first row of this wave
   const int row = rows0 + n;
   const bool row_ok = row < it.rows_total;
 
@@ -888,19 +918,36 @@ __device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, u
   ld.pf0 = unit_at(units, it, 12 + (ld.s0 & 3));
   ld.pf1 = unit_at(units, it, 12 + (ld.s1 & 3));
 
-  int t = 0;
-  for (; t + 3 < vs.t_full; t += 4) {
-    wide_step<D, 0, false>(a, it, vs, ld, smem, t, kx, voff0);
-    wide_step<D, 1, false>(a, it, vs, ld, smem, t + 1, kx, voff0);
-    wide_step<D, 2, false>(a, it, vs, ld, smem, t + 2, kx, voff0);
-    wide_step<D, 3, false>(a, it, vs, ld, smem, t + 3, kx, voff0);
-  }
-  for (; t < vs.t_full; ++t) wide_step<D, -1, false>(a, it, vs, ld, smem, t, kx, voff0);
-  for (; t < ntiles; ++t) wide_step<D, -1, true>(a, it, vs, ld, smem, t, kx, voff0);
+  if (split) wide_loop<D, true>(a, it, vs, ld, smem, kx, voff0, kh_only);
+  else wide_loop<D, false>(a, it, vs, ld, smem, kx, voff0, kh_only);
 
-  if (!vs.wave_on) return;
+  // the two halves of a shared row block merge through LDS (the ring is free now): the key-half-1
+  // wave leaves its state, the key-half-0 wave combines and writes
+  constexpr int NR = VS::ND * 16;  // accumulator floats per lane
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + (split ? ((w - nfull) >> 1) : 0) * (64 * (NR + 2));
+  if (kh_only == 1 && vs.wave_on) {
+#pragma unroll
+    for (int db = 0; db < VS::ND; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(red + ((db * 4 + q) * 64 + lane) * 4) =
+            f32x4{vs.acc_o[db][4 * q], vs.acc_o[db][4 * q + 1], vs.acc_o[db][4 * q + 2], vs.acc_o[db][4 * q + 3]};
+    red[NR * 64 + lane] = vs.m_run;
+    red[NR * 64 + 64 + lane] = vs.l_run;
+  }
+  __syncthreads();
+  if (kh_only == 1 || !vs.wave_on) return;
+  float M = vs.m_run, f0 = 1.f, f1 = 0.f, l_own = vs.l_run;
+  if (split) {
+    const float m1 = red[NR * 64 + lane], l1 = red[NR * 64 + 64 + lane];
+    M = fmaxf(vs.m_run, m1);
+    f0 = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - M);
+    f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    l_own = f0 * vs.l_run + f1 * l1;
+  }
   // the row's keys are split over the two 32-lane halves (tokens 8 h .. 8 h + 7 of each page)
-  const float l_tot = half_swap_sum(vs.l_run);
+  const float l_tot = half_swap_sum(l_own);
   if (!row_ok) return;
   bool partial;
   float* dst = out_row<D>(a, it, row, &partial);
@@ -909,12 +956,12 @@ __device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, u
   for (int db = 0; db < VS::ND; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4 o = f32x4{vs.acc_o[db][4 * q], vs.acc_o[db][4 * q + 1], vs.acc_o[db][4 * q + 2],
-                            vs.acc_o[db][4 * q + 3]} * inv;
-      *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q + 4 * h) = o;
+      f32x4 o = f32x4{vs.acc_o[db][4 * q], vs.acc_o[db][4 * q + 1], vs.acc_o[db][4 * q + 2], vs.acc_o[db][4 * q + 3]};
+      if (split) o = f0 * o + f1 * *reinterpret_cast<const f32x4*>(red + ((db * 4 + q) * 64 + lane) * 4);
+      *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q + 4 * h) = o * inv;
     }
   if (partial && h == 0) {
-    dst[D] = vs.m_run;
+    dst[D] = M;
     dst[D + 1] = l_tot;
   }
 }
@@ -1849,7 +1896,8 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
     // two per wave
     if (has_d || args.vwaves < 4 || args.vwaves > kWideMaxWaves)
       return fail(VC_EINVAL, "internal: bad wide verify plan");
-    const dim3 block(64 * args.vwaves);
+    int nfull;
+    const dim3 block(64 * wide_waves(args.vwaves, &nfull));
     if (head_dim == 128) hipLaunchKernelGGL(verify_wide_kernel<128>, grid, block, 0, stream, args);
     else hipLaunchKernelGGL(verify_wide_kernel<64>, grid, block, 0, stream, args);
   } else if (head_dim == 128) {

@@ -83,6 +83,21 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
 // Largest wide-verify work-group: 12 waves (3 per SIMD), 384 query rows.
 constexpr int kWideMaxWaves = 12;
 
+// Waves of a wide verify work-group for nrb 32-row blocks per item.  Waves are dealt to the 4
+// SIMDs in turn, so nrb = 4q + 1 or 4q + 2 whole-block waves would leave one or two SIMDs a wave
+// more than the others; instead the last nrb - 4q blocks are split by key half over two waves
+// each, and every SIMD carries at most q + 1/2 waves of work.  Returns the waves and sets *nfull
+// (the waves that own a whole block: waves nfull + 2j and nfull + 2j + 1 share block nfull + j).
+__host__ __device__ inline int wide_waves(int nrb, int* nfull) {
+  const int q = nrb / 4, rem = nrb % 4;
+  if (q >= 1 && (rem == 1 || rem == 2) && 4 * q + 2 * rem <= kWideMaxWaves) {
+    *nfull = 4 * q;
+    return 4 * q + 2 * rem;
+  }
+  *nfull = nrb;
+  return nrb;
+}
+
 // Context pages of one work item are capped so that their block ids fit the kernels' LDS.
 constexpr int kMaxChunkPages = 2048;
 
