@@ -11,9 +11,9 @@
 // the smallest index whose prefix sum exceeds u times the total weight (inverse CDF).  Uniforms
 // are inputs: the caller owns the random numbers.
 //
-// One work-group per row (sampling) or per drafted block (accept).  A draw sums contiguous
-// chunks of the vocabulary per thread, scans the chunk sums, and lets the thread whose chunk
-// holds the crossing walk it.
+// One work-group per row (sampling) or per drafted block (accept: each wave decides whole slots,
+// then the work-group draws once).  A draw sums contiguous chunks of the vocabulary per thread,
+// scans the chunk sums, and lets the thread whose chunk holds the crossing walk it.
 #include <limits.h>
 #include <math.h>
 
@@ -23,18 +23,21 @@ namespace vc {
 
 namespace {
 
-constexpr int kSThreads = 256;
-constexpr int kSWaves = kSThreads / 64;
+constexpr int kSThreads = 256;    // sampling: one work-group per row
+constexpr int kAThreads = 1024;   // accept: one work-group of 16 waves per drafted block
 
+template <int NT>
 struct SampleLds {
-  double part[kSWaves];
-  int ipart[kSWaves];
-  double chunk[kSThreads];  // chunk sums, then their exclusive prefix
+  static constexpr int NW = NT / 64;
+  double part[NW];  // per-wave partials (reductions; the draw's exclusive prefix of wave sums)
+  int ipart[NW];
   double total;
   int flag;
+  int keep[VC_MAX_ROWS];  // accept: keep decision of each slot
 };
 
-__device__ double block_sum(double v, SampleLds& s) {
+template <int NT>
+__device__ double block_sum(double v, SampleLds<NT>& s) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   __syncthreads();
@@ -42,11 +45,12 @@ __device__ double block_sum(double v, SampleLds& s) {
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int i = 0; i < kSWaves; ++i) t += s.part[i];
+  for (int i = 0; i < SampleLds<NT>::NW; ++i) t += s.part[i];
   return t;
 }
 
-__device__ double block_max(double v, SampleLds& s) {
+template <int NT>
+__device__ double block_max(double v, SampleLds<NT>& s) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
   __syncthreads();
@@ -54,11 +58,12 @@ __device__ double block_max(double v, SampleLds& s) {
   __syncthreads();
   double t = s.part[0];
 #pragma unroll
-  for (int i = 1; i < kSWaves; ++i) t = fmax(t, s.part[i]);
+  for (int i = 1; i < SampleLds<NT>::NW; ++i) t = fmax(t, s.part[i]);
   return t;
 }
 
-__device__ int block_min_int(int v, SampleLds& s) {
+template <int NT>
+__device__ int block_min_int(int v, SampleLds<NT>& s) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
   __syncthreads();
@@ -66,11 +71,12 @@ __device__ int block_min_int(int v, SampleLds& s) {
   __syncthreads();
   int t = s.ipart[0];
 #pragma unroll
-  for (int i = 1; i < kSWaves; ++i) t = min(t, s.ipart[i]);
+  for (int i = 1; i < SampleLds<NT>::NW; ++i) t = min(t, s.ipart[i]);
   return t;
 }
 
-__device__ int block_max_int(int v, SampleLds& s) {
+template <int NT>
+__device__ int block_max_int(int v, SampleLds<NT>& s) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
   __syncthreads();
@@ -78,7 +84,7 @@ __device__ int block_max_int(int v, SampleLds& s) {
   __syncthreads();
   int t = s.ipart[0];
 #pragma unroll
-  for (int i = 1; i < kSWaves; ++i) t = max(t, s.ipart[i]);
+  for (int i = 1; i < SampleLds<NT>::NW; ++i) t = max(t, s.ipart[i]);
   return t;
 }
 
@@ -89,38 +95,62 @@ struct Softmax {
   __device__ double p(int k) const { return exp(((double)z[k] - m) / t) / s; }
 };
 
-__device__ Softmax row_softmax(const float* z, int vocab, double t, SampleLds& s) {
+template <int NT>
+__device__ Softmax row_softmax(const float* z, int vocab, double t, SampleLds<NT>& s) {
   double mx = -INFINITY;
-  for (int k = threadIdx.x; k < vocab; k += kSThreads) mx = fmax(mx, (double)z[k]);
+  for (int k = threadIdx.x; k < vocab; k += NT) mx = fmax(mx, (double)z[k]);
   Softmax r{z, block_max(mx, s), 1.0, t};
   double e = 0.0;
-  for (int k = threadIdx.x; k < vocab; k += kSThreads) e += exp(((double)z[k] - r.m) / t);
+  for (int k = threadIdx.x; k < vocab; k += NT) e += exp(((double)z[k] - r.m) / t);
   r.s = block_sum(e, s);
   return r;
 }
 
-// Inverse-CDF draw with uniform u from the non-negative weights w(k), k < vocab.
-template <class W>
-__device__ int block_draw(const W& w, int vocab, double u, SampleLds& s) {
-  const int per = (vocab + kSThreads - 1) / kSThreads;
+// The same softmax statistics computed by one wave alone (no work-group synchronisation).
+__device__ Softmax wave_softmax(const float* z, int vocab, double t) {
+  const int lane = threadIdx.x & 63;
+  double mx = -INFINITY;
+  for (int k = lane; k < vocab; k += 64) mx = fmax(mx, (double)z[k]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  double e = 0.0;
+  for (int k = lane; k < vocab; k += 64) e += exp(((double)z[k] - mx) / t);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) e += __shfl_xor(e, o);
+  return Softmax{z, mx, e, t};
+}
+
+// Inverse-CDF draw with uniform u from the non-negative weights w(k), k < vocab.  Each thread
+// sums a contiguous chunk; the chunk sums are scanned within each wave (shuffles) and across the
+// waves; the thread whose chunk holds the crossing walks it.
+template <int NT, class W>
+__device__ int block_draw(const W& w, int vocab, double u, SampleLds<NT>& s) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (vocab + NT - 1) / NT;
   const int k0 = min((int)threadIdx.x * per, vocab), k1 = min(k0 + per, vocab);
   double cs = 0.0;
   for (int k = k0; k < k1; ++k) cs += w(k);
+  double inc = cs;  // inclusive scan of the chunk sums within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
   __syncthreads();
-  s.chunk[threadIdx.x] = cs;
+  if (lane == 63) s.part[wv] = inc;
   __syncthreads();
   if (threadIdx.x == 0) {
     double run = 0.0;
-    for (int i = 0; i < kSThreads; ++i) {
-      const double c = s.chunk[i];
-      s.chunk[i] = run;
+    for (int i = 0; i < SampleLds<NT>::NW; ++i) {
+      const double c = s.part[i];
+      s.part[i] = run;
       run += c;
     }
     s.total = run;
   }
   __syncthreads();
   const double target = u * s.total;
-  double run = s.chunk[threadIdx.x];
+  double run = s.part[wv] + (inc - cs);
   int found = INT_MAX, last = -1;
   for (int k = k0; k < k1; ++k) {
     const double wk = w(k);
@@ -135,43 +165,60 @@ __device__ int block_draw(const W& w, int vocab, double u, SampleLds& s) {
 
 __global__ __launch_bounds__(kSThreads) void sample_kernel(int vocab, double t, const float* logits,
                                                            const double* u, int32_t* tokens) {
-  __shared__ SampleLds s;
+  __shared__ SampleLds<kSThreads> s;
   const int row = blockIdx.x;
   const Softmax sm = row_softmax(logits + (int64_t)row * vocab, vocab, t, s);
   const int tok = block_draw([&](int k) { return sm.p(k); }, vocab, u[row], s);
   if (threadIdx.x == 0) tokens[row] = tok;
 }
 
-__global__ __launch_bounds__(kSThreads) void accept_sampled_kernel(int max_x, int max_xv, int vocab, double t,
+// One drafted block: every slot's keep test at once (one wave per slot, 16 slots at a time),
+// then the first slot not kept draws from the residual, or, with every slot kept, the
+// verifier's extra row gives the bonus token.
+__global__ __launch_bounds__(kAThreads) void accept_sampled_kernel(int max_x, int max_xv, int vocab, double t,
                                                                    const int32_t* x, const int32_t* xv,
                                                                    const float* dl, const float* vl,
                                                                    const int32_t* dtok, const double* ua,
                                                                    const double* ur, int32_t* alen,
                                                                    int32_t* ntok) {
-  __shared__ SampleLds s;
+  __shared__ SampleLds<kAThreads> s;
+  constexpr int NW = SampleLds<kAThreads>::NW;
   const int inst = blockIdx.x;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nx = min(max(x[inst], 0), max_x), nxv = min(max(xv[inst], 0), max_xv);
   const int nslots = min(nx, nxv);  // a slot needs its verifier row
-  for (int i = 0; i < nslots; ++i) {
-    const Softmax pl = row_softmax(dl + ((int64_t)inst * max_x + i) * vocab, vocab, t, s);
-    const Softmax pf = row_softmax(vl + ((int64_t)inst * max_xv + i) * vocab, vocab, t, s);
-    if (threadIdx.x == 0) {
+  for (int i = wv; i < nslots; i += NW) {
+    const Softmax pl = wave_softmax(dl + ((int64_t)inst * max_x + i) * vocab, vocab, t);
+    const Softmax pf = wave_softmax(vl + ((int64_t)inst * max_xv + i) * vocab, vocab, t);
+    if (lane == 0) {
       const int tok = dtok[(int64_t)inst * max_x + i];
       // a token outside the vocabulary is never kept
-      s.flag = (tok >= 0 && tok < vocab) ? (ua[(int64_t)inst * max_x + i] * pl.p(tok) < pf.p(tok)) : 0;
+      s.keep[i] = (tok >= 0 && tok < vocab) ? (ua[(int64_t)inst * max_x + i] * pl.p(tok) < pf.p(tok)) : 0;
     }
-    __syncthreads();
-    const bool keep = s.flag != 0;
-    __syncthreads();
-    if (keep) continue;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int first = nslots;
+    for (int i = 0; i < nslots; ++i)
+      if (!s.keep[i]) {
+        first = i;
+        break;
+      }
+    s.flag = first;
+  }
+  __syncthreads();
+  const int first = s.flag;
+  if (first < nslots) {
+    const Softmax pl = row_softmax(dl + ((int64_t)inst * max_x + first) * vocab, vocab, t, s);
+    const Softmax pf = row_softmax(vl + ((int64_t)inst * max_xv + first) * vocab, vocab, t, s);
     auto resid = [&](int k) { return fmax(pf.p(k) - pl.p(k), 0.0); };
     double r = 0.0;
-    for (int k = threadIdx.x; k < vocab; k += kSThreads) r += resid(k);
+    for (int k = threadIdx.x; k < vocab; k += kAThreads) r += resid(k);
     r = block_sum(r, s);
-    const double u = ur[(int64_t)inst * (max_x + 1) + i];
+    const double u = ur[(int64_t)inst * (max_x + 1) + first];
     const int tok = r > 0.0 ? block_draw(resid, vocab, u, s) : block_draw([&](int k) { return pf.p(k); }, vocab, u, s);
     if (threadIdx.x == 0) {
-      alen[inst] = i;
+      alen[inst] = first;
       ntok[inst] = tok;
     }
     return;
@@ -223,7 +270,7 @@ int vc_accept_sampled(int n_inst, int max_x, int max_xv, int vocab, float temper
   if (!x || !xv || !draft_logits || !verify_logits || !draft_tok || !u_accept || !u_resample || !accept_len ||
       !next_tok)
     return fail(VC_EINVAL, "NULL argument");
-  hipLaunchKernelGGL(accept_sampled_kernel, dim3(n_inst), dim3(kSThreads), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(accept_sampled_kernel, dim3(n_inst), dim3(kAThreads), 0, static_cast<hipStream_t>(stream),
                      max_x, max_xv, vocab, (double)temperature, x, xv, draft_logits, verify_logits, draft_tok,
                      u_accept, u_resample, accept_len, next_tok);
   return hip_check(hipGetLastError(), "sampled accept launch");
