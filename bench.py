@@ -42,6 +42,24 @@ def measured_traffic(config: str, kind: str):
     return None if not k else k.get("bytes_per_launch")
 
 
+def host_info():
+    """The host the oracle ran on: CPU model, logical CPUs usable by this process, RAM."""
+    model, ram_gb = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        with open("/proc/meminfo") as f:
+            kb = next((int(ln.split()[1]) for ln in f if ln.startswith("MemTotal")), None)
+        ram_gb = None if kb is None else round(kb / 2**20, 1)
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": usable, "ram_gib": ram_gb}
+
+
 def cpu_baseline(cfg, budget_s: float):
     """The oracle, untuned, on a bounded sample of the same round, scaled to the whole round:
     (request, layer, kv head) units of the verify pass plus all x draft steps are timed until
@@ -292,7 +310,7 @@ def main():
         round_s, threads, sample = cpu_baseline(cfg, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(round_bytes / round_s / 1e12, 8), "unit": "TB/s",
                                "cores": threads, "kind": "oracle", "sample": sample,
-                               "round_seconds_scaled": round(round_s, 1)}
+                               "round_seconds_scaled": round(round_s, 1), "host": host_info()}
     print(json.dumps(out), flush=True)
 
 
