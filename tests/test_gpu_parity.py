@@ -118,7 +118,7 @@ def test_verify_parity(name):
 def wide_cfg(kind):
     """Verify launches of more than 128 query rows (x * G) per (layer, kv head)."""
     c4 = C.get("C4")
-    if kind == "g8_x17":    # 136 rows: 5 waves, three of which load two ring slots
+    if kind == "g8_x17":    # 136 rows = 5 blocks: 4 whole-block waves and 2 half waves
         return C.scaled(c4, L=1, B=2, n=900, x=17)
     if kind == "g8_x64":    # 512 rows: two row groups of 256 (8 waves)
         return C.scaled(c4, L=1, B=1, n=700, x=64)
@@ -127,11 +127,19 @@ def wide_cfg(kind):
                 C.Request(ctx_len=333, x=3, comp=C.COMP_DROP, recent=64, top=333 // 4)]
         return C.Config("wide-g16-d64", 41, L=1, Hq=32, Hkv=2, d=64, reqs=reqs, wu_width=512,
                         vocab=1024)
+    if kind == "g8_d64_x40":  # G = 8, d = 64: 40 * 8 = 320 rows = 10 blocks, the last two split by
+        # key half over four waves (12 waves); the second request (24 * 8 = 192 rows) leaves the
+        # split waves without rows
+        reqs = [C.Request(ctx_len=777, x=40, comp=C.COMP_DROP, recent=64, top=777 // 4),
+                C.Request(ctx_len=401, x=24, comp=C.COMP_DROP, recent=64, top=401 // 4)]
+        return C.Config("wide-g8-d64", 42, L=2, Hq=16, Hkv=2, d=64, reqs=reqs, wu_width=1024,
+                        vocab=1024)
     raise KeyError(kind)
 
 
 @pytest.mark.parametrize("kind,split_pages", [("g8_x17", 0), ("g8_x17", 8), ("g8_x64", 0),
-                                              ("g16_d64", 0), ("g16_d64", 4)])
+                                              ("g16_d64", 0), ("g16_d64", 4),
+                                              ("g8_d64_x40", 0), ("g8_d64_x40", 8)])
 def test_wide_verify_parity(kind, split_pages):
     """Every output element of the wide verify work-groups (one wave per 32 rows, 5 to 12 waves)
     against the oracle, unsplit and with context splits of 2 and 1 tiles (partials + merge)."""
