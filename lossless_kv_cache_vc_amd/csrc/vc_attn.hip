@@ -534,13 +534,17 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
 // into key stage t % 4, V(t + 3) into value stage (t - 1) % 4), score tile t + 1 into s_nxt (the
 // last tile scores a stale stage, unused) and consume tile t.  STC >= 0: t % 4 == STC known at
 // compile time.
-template <int D, int STC, bool MASK>
+template <int D, int STC, bool MASK, bool STEADY = false>
 __device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs,
                                             uint8_t* smem, int t, f32x16& s_cur, f32x16& s_nxt) {
   const int st = STC >= 0 ? STC : (t & (kVStages - 1));
   const int ntiles = vs.ntiles;
-  // keys: K(t + 1) must have landed (K issued up to t + 3); values: V(t) (V issued up to t + 3)
-  if (vs.kwave) {
+  // keys: K(t + 1) must have landed (K issued up to t + 3); values: V(t) (V issued up to t + 3).
+  // STEADY: t + 4 < ntiles, so both waits leave three tiles in flight and the refill is issued.
+  if constexpr (STEADY) {
+    if (vs.kwave) wait_tiles<D>(2);
+    else wait_tiles<D>(3);
+  } else if (vs.kwave) {
     if (t + 1 < ntiles) wait_tiles<D>(min(2, ntiles - t - 2));
   } else {
     wait_tiles<D>(min(3, ntiles - t - 1));
@@ -551,7 +555,7 @@ __device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it
   // then read the unit for the next tile's load
   const int vst = vs.vst;
   const int vst4 = vst == 0 ? kVVStages - 1 : vst - 1;  // (t + 4) % 5
-  if (t + 4 < ntiles) verify_issue<D>(a, it, vs, smem, t + 4, vs.kwave ? st : vst4, vs.pf_unit);
+  if (STEADY || t + 4 < ntiles) verify_issue<D>(a, it, vs, smem, t + 4, vs.kwave ? st : vst4, vs.pf_unit);
   {
     const int ipn = 4 * (t + 5) + vs.ps;
     vs.pf_unit = ipn < it.nctx ? vs.units[ipn] : -1;
@@ -676,6 +680,13 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
   // full tiles (no masking) four at a time, so ring stages are compile-time and the scores
   // alternate between s_a and s_b without register copies; then the rest, with masking
   int t = 0;
+  // steady state: every step of the group issues its refill (t + 7 < ntiles)
+  for (; t + 3 < vs.t_full && t + 7 < ntiles; t += 4) {
+    verify_step<D, 0, false, true>(a, it, vs, smem, t, s_a, s_b);
+    verify_step<D, 1, false, true>(a, it, vs, smem, t + 1, s_b, s_a);
+    verify_step<D, 2, false, true>(a, it, vs, smem, t + 2, s_a, s_b);
+    verify_step<D, 3, false, true>(a, it, vs, smem, t + 3, s_b, s_a);
+  }
   for (; t + 3 < vs.t_full; t += 4) {
     verify_step<D, 0, false>(a, it, vs, smem, t, s_a, s_b);
     verify_step<D, 1, false>(a, it, vs, smem, t + 1, s_b, s_a);
