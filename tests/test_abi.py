@@ -82,6 +82,21 @@ def test_host_validation_rejects_bad_arguments():
     _expect(vc.VC_EINVAL, lambda: vc.logits(4, 8, 8, t, 4, t, t, 0))
 
 
+def test_empty_launches_do_nothing():
+    """Launches with nothing to compute return VC_OK without touching the device (this runs
+    without a GPU): no requests, no rows of logits, no accept instances."""
+    t = _FakeTensor(0x1000)
+    vc.verify_attn(_shape(), [], t, t, t, _pool(), t, None, 0, 0)
+    vc.draft_attn(_shape(), [], t, t, t, _pool(), t, None, 0, 0)
+    vc.attn_mixed(_shape(), [], t, t, t, [_pool(), _pool()], t, None, 0, 0)
+    vc.logits(0, 8, 8, t, 8, t, t, 0)
+    vc.accept(0, 4, 4, 16, t, t, t, t, t, t, t, t, 0)
+    assert vc.attn_workspace_size(_shape(), []) == 0
+    # rows must be at least 1 and fit the drafted-block capacity even when nothing else is wrong
+    _expect(vc.VC_EINVAL, lambda: vc.verify_attn(_shape(), [vc.Req(0, 0, 100, 0, 0, 0, vc.VC_VERIFY)],
+                                                 t, t, t, _pool(), t, None, 0, 0))
+
+
 def test_workspace_size_accounts_for_splits():
     shp = _shape()
     r = vc.Req(0, 0, 16 * 100, 0, 0, 8, vc.VC_VERIFY)
