@@ -1750,12 +1750,14 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 }
 
 // Work item -> (request, row group, split, kv head, layer).  Work-groups are dealt round-robin
-// over the 8 XCDs; consecutive items are mapped to one XCD so that items that share K/V (row
-// groups of one unit) run on the same L2.
+// over the 8 XCDs.  With xcd_ranges, consecutive items are mapped to one XCD so that items that
+// share K/V (row groups of one unit) run on the same L2; without, work-group b takes item b, so
+// every request of a ragged batch is spread over all XCDs instead of each XCD holding a range of
+// requests of unequal cost.
 __device__ __forceinline__ bool decode_item(const AttnArgs& a, ItemCtx* it, int* rg) {
   const int b = blockIdx.x;
   const int per = a.nitems_pad >> 3;
-  const int item = (b & 7) * per + (b >> 3);
+  const int item = a.xcd_ranges ? (b & 7) * per + (b >> 3) : b;
   if (item >= a.nitems) return false;
   int r = 0;
   for (int i = 1; i < a.nreq; ++i)

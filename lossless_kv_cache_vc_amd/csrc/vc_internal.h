@@ -62,6 +62,8 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(d)
   int32_t vwaves;    // verify work-group: 0 = 8 waves over 128-row groups; else that many
                      // waves, one per 32 rows, over groups of 32 * vwaves rows (wide verify)
+  int32_t xcd_ranges;  // 1: each XCD takes a contiguous range of items (row groups of a unit
+                       // share an L2); 0: work-group b takes item b (ragged batches)
   ReqDev reqs[kMaxReqs];
 };
 
