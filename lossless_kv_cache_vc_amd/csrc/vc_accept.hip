@@ -104,12 +104,88 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(int max_x, int max_
 // A work-group of 4 waves computes a 128 x 128 tile of z, each wave 64 x 64 (2 x 2 blocks of
 // 32 x 32, v_mfma_f32_32x32x16_bf16), over K steps of 32 staged in LDS: o as hi and lo [m][k],
 // W_u transposed to [n][k], so every MFMA operand is one 16-byte LDS read; rows are padded to 40
-// bf16 (80 bytes) so the reads of a 32-lane half fall on distinct banks.  VEC: o rows, W_u rows
-// and the bases allow 16-byte global loads.
+// bf16 (80 bytes) so the reads of a 32-lane half fall on distinct banks.  The next K step's
+// global loads are issued into registers before this step's MFMAs.  VEC: o rows, W_u rows and
+// the bases allow 16-byte global loads.
 constexpr int kLM = 128, kLN = 128, kLK = 32, kLPad = 40;
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// One K step's global data of a thread: 4 runs of 4 consecutive o elements (rows mm, k kq..kq+3)
+// and two k rows of 8 consecutive W_u entries (k 2kp, 2kp + 1; n nq..nq+7).
+struct LogitsTile {
+  float o[4][4];
+  uint32_t w[2][4];
+};
+
+template <bool VEC>
+__device__ __forceinline__ void logits_fetch(LogitsTile& t, int rows, int width, int vocab, const float* o,
+                                             int64_t ld_o, const uint16_t* wu, int m0, int n0, int k0) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    const int mm = e / (kLK / 4), kq = (e % (kLK / 4)) * 4;
+    const int gm = m0 + mm, gk = k0 + kq;
+    if constexpr (VEC) {  // width % 4 == 0: the 4 elements are all inside or all outside
+      const f32x4 v = (gm < rows && gk < width) ? *reinterpret_cast<const f32x4*>(o + (int64_t)gm * ld_o + gk)
+                                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t.o[i][j] = v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t.o[i][j] = (gm < rows && gk + j < width) ? o[(int64_t)gm * ld_o + gk + j] : 0.f;
+    }
+  }
+  const int kp = tid % (kLK / 2), nq = (tid / (kLK / 2)) * 8;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int gk = k0 + 2 * kp + r, gn = n0 + nq;
+    if constexpr (VEC) {  // vocab % 8 == 0
+      const u32x4 v = (gk < width && gn < vocab) ? *reinterpret_cast<const u32x4*>(wu + (int64_t)gk * vocab + gn)
+                                                 : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t.w[r][j] = v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (gk < width && gn + 2 * j < vocab) ? wu[(int64_t)gk * vocab + gn + 2 * j] : 0;
+        const uint32_t hi = (gk < width && gn + 2 * j + 1 < vocab) ? wu[(int64_t)gk * vocab + gn + 2 * j + 1] : 0;
+        t.w[r][j] = lo | (hi << 16);
+      }
+    }
+  }
+}
+
+// o as bf16 hi and lo parts [m][k]; W_u transposed [n][k], the thread's two k rows packed into
+// one 32-bit store per n (consecutive threads take consecutive k pairs: distinct banks)
+__device__ __forceinline__ void logits_stage(const LogitsTile& t, uint16_t* s_hi, uint16_t* s_lo, uint16_t* s_w) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    const int mm = e / (kLK / 4), kq = (e % (kLK / 4)) * 4;
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const uint16_t h0 = bf16_bits(t.o[i][j]), h1 = bf16_bits(t.o[i][j + 1]);
+      const float r0 = t.o[i][j] - __builtin_bit_cast(float, (uint32_t)h0 << 16);
+      const float r1 = t.o[i][j + 1] - __builtin_bit_cast(float, (uint32_t)h1 << 16);
+      hi[j >> 1] = h0 | ((uint32_t)h1 << 16);
+      lo[j >> 1] = bf16_bits(r0) | ((uint32_t)bf16_bits(r1) << 16);
+    }
+    *reinterpret_cast<u32x2*>(s_hi + mm * kLPad + kq) = u32x2{hi[0], hi[1]};
+    *reinterpret_cast<u32x2*>(s_lo + mm * kLPad + kq) = u32x2{lo[0], lo[1]};
+  }
+  const int kp = tid % (kLK / 2), nq = (tid / (kLK / 2)) * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w0 = (t.w[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t w1 = (t.w[1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    *reinterpret_cast<uint32_t*>(s_w + (nq + j) * kLPad + 2 * kp) = w0 | (w1 << 16);
+  }
 }
 
 template <bool VEC>
@@ -118,7 +194,7 @@ __global__ __launch_bounds__(256) void logits_kernel(int rows, int width, int vo
   __shared__ __attribute__((aligned(16))) uint16_t s_hi[kLM * kLPad];
   __shared__ __attribute__((aligned(16))) uint16_t s_lo[kLM * kLPad];
   __shared__ __attribute__((aligned(16))) uint16_t s_w[kLN * kLPad];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int m0 = blockIdx.y * kLM, n0 = blockIdx.x * kLN;
   const int wm = (w & 1) * 64, wn = (w >> 1) * 64;  // this wave's 64 x 64 part of the tile
   const int r32 = lane & 31, kh = lane >> 5;
@@ -127,57 +203,13 @@ __global__ __launch_bounds__(256) void logits_kernel(int rows, int width, int vo
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  LogitsTile t;
+  logits_fetch<VEC>(t, rows, width, vocab, o, ld_o, wu, m0, n0, 0);
   for (int k0 = 0; k0 < width; k0 += kLK) {
-    // o: 128 rows x 32 k, 4 consecutive k per thread and step
-#pragma unroll
-    for (int e = tid; e < kLM * kLK / 4; e += 256) {
-      const int mm = e / (kLK / 4), kq = (e % (kLK / 4)) * 4;
-      const int gm = m0 + mm, gk = k0 + kq;
-      float v[4];
-      if constexpr (VEC) {  // width % 4 == 0: the 4 elements are all inside or all outside
-        const f32x4 t = (gm < rows && gk < width) ? *reinterpret_cast<const f32x4*>(o + (int64_t)gm * ld_o + gk)
-                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = t[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = (gm < rows && gk + j < width) ? o[(int64_t)gm * ld_o + gk + j] : 0.f;
-      }
-      uint32_t hi[2], lo[2];
-#pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const uint16_t h0 = bf16_bits(v[j]), h1 = bf16_bits(v[j + 1]);
-        const float r0 = v[j] - __builtin_bit_cast(float, (uint32_t)h0 << 16);
-        const float r1 = v[j + 1] - __builtin_bit_cast(float, (uint32_t)h1 << 16);
-        hi[j >> 1] = h0 | ((uint32_t)h1 << 16);
-        lo[j >> 1] = bf16_bits(r0) | ((uint32_t)bf16_bits(r1) << 16);
-      }
-      *reinterpret_cast<u32x2*>(s_hi + mm * kLPad + kq) = u32x2{hi[0], hi[1]};
-      *reinterpret_cast<u32x2*>(s_lo + mm * kLPad + kq) = u32x2{lo[0], lo[1]};
-    }
-    // W_u: 32 k x 128 n, 8 consecutive n per thread and step, stored transposed ([n][k]);
-    // consecutive threads take consecutive k, so the 2-byte LDS writes spread over the banks
-#pragma unroll
-    for (int e = tid; e < kLK * kLN / 8; e += 256) {
-      const int kk = e % kLK, nq = (e / kLK) * 8;
-      const int gk = k0 + kk, gn = n0 + nq;
-      uint16_t v[8];
-      if constexpr (VEC) {  // vocab % 8 == 0
-        const u32x4 t = (gk < width && gn < vocab) ? *reinterpret_cast<const u32x4*>(wu + (int64_t)gk * vocab + gn)
-                                                   : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = (uint16_t)(t[j] & 0xFFFFu);
-          v[2 * j + 1] = (uint16_t)(t[j] >> 16);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (gk < width && gn + j < vocab) ? wu[(int64_t)gk * vocab + gn + j] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s_w[(nq + j) * kLPad + kk] = v[j];
-    }
+    logits_stage(t, s_hi, s_lo, s_w);
     __syncthreads();
+    // the next K step's loads are in flight while this step's MFMAs run
+    if (k0 + kLK < width) logits_fetch<VEC>(t, rows, width, vocab, o, ld_o, wu, m0, n0, k0 + kLK);
 #pragma unroll
     for (int ks = 0; ks < kLK / 16; ++ks) {
       const int kc = ks * 16 + kh * 8;  // lane's 8 k of this 16-k step
