@@ -128,8 +128,20 @@ __device__ int block_draw(const W& w, int vocab, double u, SampleLds<NT>& s) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int per = (vocab + NT - 1) / NT;
   const int k0 = min((int)threadIdx.x * per, vocab), k1 = min(k0 + per, vocab);
+  // chunks of up to kCache weights are evaluated once and kept in registers for the walk
+  constexpr int kCache = 16;
+  const bool cached = per <= kCache;
+  double wc[kCache];
   double cs = 0.0;
-  for (int k = k0; k < k1; ++k) cs += w(k);
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+      wc[i] = k0 + i < k1 ? w(k0 + i) : 0.0;
+      cs += wc[i];
+    }
+  } else {
+    for (int k = k0; k < k1; ++k) cs += w(k);
+  }
   double inc = cs;  // inclusive scan of the chunk sums within the wave
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -152,11 +164,22 @@ __device__ int block_draw(const W& w, int vocab, double u, SampleLds<NT>& s) {
   const double target = u * s.total;
   double run = s.part[wv] + (inc - cs);
   int found = INT_MAX, last = -1;
-  for (int k = k0; k < k1; ++k) {
-    const double wk = w(k);
-    run += wk;
-    if (wk > 0.0) last = k;
-    if (found == INT_MAX && run > target) found = k;
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+      if (k0 + i >= k1) break;
+      const double wk = wc[i];
+      run += wk;
+      if (wk > 0.0) last = k0 + i;
+      if (found == INT_MAX && run > target) found = k0 + i;
+    }
+  } else {
+    for (int k = k0; k < k1; ++k) {
+      const double wk = w(k);
+      run += wk;
+      if (wk > 0.0) last = k;
+      if (found == INT_MAX && run > target) found = k;
+    }
   }
   found = block_min_int(found, s);
   if (found == INT_MAX) found = block_max_int(last, s);  // rounding left u * total above every prefix
