@@ -402,9 +402,10 @@ __device__ __forceinline__ f32x16 verify_scores(const uint8_t* smem, int st, con
   return acc;
 }
 
-// Online softmax of one tile's scores and O^T += V^T P^T from value stage `st`.  MASK: the tile
-// holds a partial, missing or drafted-block page (per-key visibility and value masking);
-// otherwise every key of the tile is a visible context key.
+// Online softmax of one key half's scores and O^T += V^T P^T from value stage `vst` (the wide
+// verify: its waves score a half and consume it in turn).  MASK: the tile holds a partial,
+// missing or drafted-block page (per-key visibility and value masking); otherwise every key of
+// the tile is a visible context key.
 template <int D, bool MASK>
 __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>& vs, const uint8_t* smem,
                                                int t, int vst, f32x16 s_acc) {
