@@ -120,28 +120,15 @@ __device__ Softmax wave_softmax(const float* z, int vocab, double t) {
   return Softmax{z, mx, e, t};
 }
 
-// Inverse-CDF draw with uniform u from the non-negative weights w(k), k < vocab.  Each thread
-// sums a contiguous chunk; the chunk sums are scanned within each wave (shuffles) and across the
-// waves; the thread whose chunk holds the crossing walks it.
-template <int NT, class W>
-__device__ int block_draw(const W& w, int vocab, double u, SampleLds<NT>& s) {
+// Inverse-CDF draws.  Each thread owns a contiguous chunk of the vocabulary; the chunk sums are
+// scanned within each wave (shuffles) and across the waves; the thread whose chunk holds the
+// crossing walks it.  Chunks of up to kCache weights are evaluated once and kept in registers.
+constexpr int kCache = 16;
+
+// The draw over chunk weights wc[0 .. k1 - k0) of this thread (sum cs), from uniform u.
+template <int NT>
+__device__ int draw_cached(const double (&wc)[kCache], int k0, int k1, double cs, double u, SampleLds<NT>& s) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int per = (vocab + NT - 1) / NT;
-  const int k0 = min((int)threadIdx.x * per, vocab), k1 = min(k0 + per, vocab);
-  // chunks of up to kCache weights are evaluated once and kept in registers for the walk
-  constexpr int kCache = 16;
-  const bool cached = per <= kCache;
-  double wc[kCache];
-  double cs = 0.0;
-  if (cached) {
-#pragma unroll
-    for (int i = 0; i < kCache; ++i) {
-      wc[i] = k0 + i < k1 ? w(k0 + i) : 0.0;
-      cs += wc[i];
-    }
-  } else {
-    for (int k = k0; k < k1; ++k) cs += w(k);
-  }
   double inc = cs;  // inclusive scan of the chunk sums within the wave
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -164,22 +151,65 @@ __device__ int block_draw(const W& w, int vocab, double u, SampleLds<NT>& s) {
   const double target = u * s.total;
   double run = s.part[wv] + (inc - cs);
   int found = INT_MAX, last = -1;
-  if (cached) {
+#pragma unroll
+  for (int i = 0; i < kCache; ++i) {
+    if (k0 + i >= k1) break;
+    const double wk = wc[i];
+    run += wk;
+    if (wk > 0.0) last = k0 + i;
+    if (found == INT_MAX && run > target) found = k0 + i;
+  }
+  found = block_min_int(found, s);
+  if (found == INT_MAX) found = block_max_int(last, s);  // rounding left u * total above every prefix
+  return found < 0 ? 0 : found;
+}
+
+// Draw with uniform u from the non-negative weights w(k), k < vocab (the smallest index whose
+// prefix sum exceeds u times the total).
+template <int NT, class W>
+__device__ int block_draw(const W& w, int vocab, double u, SampleLds<NT>& s) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (vocab + NT - 1) / NT;
+  const int k0 = min((int)threadIdx.x * per, vocab), k1 = min(k0 + per, vocab);
+  if (per <= kCache) {
+    double wc[kCache];
+    double cs = 0.0;
 #pragma unroll
     for (int i = 0; i < kCache; ++i) {
-      if (k0 + i >= k1) break;
-      const double wk = wc[i];
-      run += wk;
-      if (wk > 0.0) last = k0 + i;
-      if (found == INT_MAX && run > target) found = k0 + i;
+      wc[i] = k0 + i < k1 ? w(k0 + i) : 0.0;
+      cs += wc[i];
     }
-  } else {
-    for (int k = k0; k < k1; ++k) {
-      const double wk = w(k);
-      run += wk;
-      if (wk > 0.0) last = k;
-      if (found == INT_MAX && run > target) found = k;
+    return draw_cached(wc, k0, k1, cs, u, s);
+  }
+  double cs = 0.0;
+  for (int k = k0; k < k1; ++k) cs += w(k);
+  double inc = cs;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
+  __syncthreads();
+  if (lane == 63) s.part[wv] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double run = 0.0;
+    for (int i = 0; i < SampleLds<NT>::NW; ++i) {
+      const double c = s.part[i];
+      s.part[i] = run;
+      run += c;
     }
+    s.total = run;
+  }
+  __syncthreads();
+  const double target = u * s.total;
+  double run = s.part[wv] + (inc - cs);
+  int found = INT_MAX, last = -1;
+  for (int k = k0; k < k1; ++k) {
+    const double wk = w(k);
+    run += wk;
+    if (wk > 0.0) last = k;
+    if (found == INT_MAX && run > target) found = k;
   }
   found = block_min_int(found, s);
   if (found == INT_MAX) found = block_max_int(last, s);  // rounding left u * total above every prefix
@@ -190,8 +220,30 @@ __global__ __launch_bounds__(kSThreads) void sample_kernel(int vocab, double t, 
                                                            const double* u, int32_t* tokens) {
   __shared__ SampleLds<kSThreads> s;
   const int row = blockIdx.x;
-  const Softmax sm = row_softmax(logits + (int64_t)row * vocab, vocab, t, s);
-  const int tok = block_draw([&](int k) { return sm.p(k); }, vocab, u[row], s);
+  const float* z = logits + (int64_t)row * vocab;
+  const int per = (vocab + kSThreads - 1) / kSThreads;
+  int tok;
+  if (per <= kCache) {
+    // one exponential per entry: the row maximum over the thread's chunk, then unnormalised
+    // weights exp((z - m) / T), drawn from directly (normalising does not move the crossing)
+    const int k0 = min((int)threadIdx.x * per, vocab), k1 = min(k0 + per, vocab);
+    double mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kCache; ++i)
+      if (k0 + i < k1) mx = fmax(mx, (double)z[k0 + i]);
+    const double m = block_max(mx, s);
+    double wc[kCache];
+    double cs = 0.0;
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+      wc[i] = k0 + i < k1 ? exp(((double)z[k0 + i] - m) / t) : 0.0;
+      cs += wc[i];
+    }
+    tok = draw_cached(wc, k0, k1, cs, u[row], s);
+  } else {
+    const Softmax sm = row_softmax(z, vocab, t, s);
+    tok = block_draw([&](int k) { return sm.p(k); }, vocab, u[row], s);
+  }
   if (threadIdx.x == 0) tokens[row] = tok;
 }
 
