@@ -45,6 +45,16 @@ def accept(draft_tok, verify_tok):
     return a, nxt
 
 
+def accept_block(draft_tok, verify_tok):
+    """(accept length a, next token) when the verifier may have given fewer rows than drafted
+    slots.  Reading: a drafted slot without a verifier row cannot be checked, so the block ends at
+    the verifier's last row and the rule above runs on the first len(verify_tok) drafted slots
+    (then a <= len(verify_tok) and next is -1 when every compared slot matched)."""
+    if len(verify_tok) < len(draft_tok):
+        return accept(list(draft_tok)[: len(verify_tok)], verify_tok)
+    return accept(draft_tok, verify_tok)
+
+
 def accept_flagged(a: int, x: int, draft_gap, verify_gap, tie_gap: float = TIE_GAP) -> bool:
     """True if the accept length depends on a near-tie row (rows 0..min(a, x-1))."""
     last = min(a, x - 1)

@@ -36,6 +36,17 @@ def test_accept_rejects_bad_lengths():
         acc.accept([1, 2, 3], [1])
 
 
+def test_short_verifier_ends_the_block():
+    """A verifier with fewer rows than drafted slots: only its rows are compared (hand cases)."""
+    assert acc.accept_block([5, 7, 9, 11], [5, 7]) == (2, -1)      # both compared slots agree
+    assert acc.accept_block([5, 7, 9, 11], [5, 6]) == (1, 6)       # mismatch inside the rows
+    assert acc.accept_block([5, 7, 9, 11], []) == (0, -1)          # no verifier row at all
+    assert acc.accept_block([5, 7, 9, 11], [4]) == (0, 4)
+    # with x or x + 1 rows it is the plain rule
+    assert acc.accept_block([5, 7], [5, 7, 3]) == (2, 3)
+    assert acc.accept_block([5, 7], [5, 8]) == (1, 8)
+
+
 def test_argmax_ties_and_gap():
     z = np.array([[0.0, 3.0, 3.0, 1.0], [5.0, -1.0, 4.5, 4.9], [2.0, 2.0, 2.0, 2.0]])
     t, gap = acc.argmax_gap(z)
