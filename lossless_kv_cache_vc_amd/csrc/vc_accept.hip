@@ -83,8 +83,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(int max_x, int max_
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int a = nx;
-    for (int i = 0; i < nx; ++i)
+    // only slots that both passes predicted are compared: a verifier with fewer rows than
+    // drafted slots (xv < x) ends the block at its last row
+    const int ncmp = min(nx, nxv);
+    int a = ncmp;
+    for (int i = 0; i < ncmp; ++i)
       if (td[i] != tv[i]) {
         a = i;
         break;

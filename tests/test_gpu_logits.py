@@ -86,3 +86,45 @@ def test_greedy_accept_matches_the_oracle(vocab):
         assert np.array_equal(dt[i, :x[i]], td) and np.all(dt[i, x[i]:] == -1)
         assert np.array_equal(vt[i, :xv[i]], tv) and np.all(vt[i, xv[i]:] == -1)
         assert (al[i], nt[i]) == oacc.accept(td, tv)
+
+
+@pytest.mark.parametrize("max_x,max_xv", [(64, 65), (40, 24)])
+def test_greedy_accept_short_verifier(max_x, max_xv):
+    """Instances whose verifier has fewer rows than drafted slots (xv < x), including a launch with
+    max_xv < max_x: only slots with a verifier row are compared, so accept_len <= xv and next_tok is
+    -1 when every compared slot agrees.  The logits rows past each instance's xv are NaN-free noise
+    with an agreeing argmax planted, so a kernel that read past xv would return a longer block."""
+    require_gpu()
+    from lossless_kv_cache_vc_amd import vc
+    print(f"greedy accept short verifier max_x={max_x} max_xv={max_xv}", flush=True)
+    rng = np.random.default_rng(max_x * 100 + max_xv)
+    n_inst, vocab = 40, 512
+    x = rng.integers(1, max_x + 1, n_inst).astype(np.int32)
+    # verifier rows: at most x + 1 (the bonus row), here mostly fewer than x
+    xv = np.minimum(np.minimum(rng.integers(0, max_x + 1, n_inst), x + 1), max_xv).astype(np.int32)
+    xv[:4] = np.minimum([0, 1, x[2] - 1, x[3] + 1], max_xv).clip(0)
+    zd = rng.standard_normal((n_inst, max_x, vocab)).astype(np.float32)
+    zv = rng.standard_normal((n_inst, max_xv, vocab)).astype(np.float32)
+    for i in range(n_inst):
+        agree = rng.integers(0, max_x + 1)   # drafted slots before `agree` match the verifier's rows
+        for j in range(min(agree, max_xv)):
+            t = rng.integers(0, vocab)
+            zd[i, j, t] = zv[i, j, t] = 10.0
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    dt = torch.empty((n_inst, max_x), dtype=torch.int32, device="cuda")
+    vt = torch.empty((n_inst, max_xv), dtype=torch.int32, device="cuda")
+    al = torch.empty(n_inst, dtype=torch.int32, device="cuda")
+    nt = torch.empty(n_inst, dtype=torch.int32, device="cuda")
+    for rep in range(2):   # the second launch, with the verifier lengths permuted, must not see
+        if rep:            # the first one's tokens
+            xv = np.minimum(np.minimum(xv[::-1], x + 1), max_xv).astype(np.int32)
+        vc.accept(n_inst, max_x, max_xv, vocab, to(x), to(xv), to(zd), to(zv), dt, vt, al, nt)
+        torch.cuda.synchronize()
+        d_, v_, a_, n_ = dt.cpu().numpy(), vt.cpu().numpy(), al.cpu().numpy(), nt.cpu().numpy()
+        for i in range(n_inst):
+            td, _ = oacc.argmax_gap(zd[i, :x[i]].astype(np.float64))
+            tv, _ = oacc.argmax_gap(zv[i, :xv[i]].astype(np.float64)) if xv[i] else (np.zeros(0, np.int64), None)
+            assert np.array_equal(d_[i, :x[i]], td)
+            assert np.array_equal(v_[i, :xv[i]], tv) and np.all(v_[i, xv[i]:] == -1)
+            assert (a_[i], n_[i]) == oacc.accept_block(td, tv), (i, x[i], xv[i])
+            assert a_[i] <= min(x[i], xv[i])
