@@ -21,6 +21,12 @@
  *   pool uses the same table.  Positions past a request's length inside its last page, and
  *   drafted-block rows past the last visible one, may hold any bits (even NaN): they never
  *   reach a result.
+ * - Page-table entries live in device memory, so the host cannot check them.  An entry of -1 is a
+ *   hole (the page is absent).  An entry below -1 or at or past num_blocks is corrupt: kernels
+ *   never dereference it (the page is treated as absent, or a write to it is skipped), and they
+ *   record it in a per-device error word that vc_check_device() reports as VC_EDEVICE.  The word
+ *   is shared by every call on the device and keeps one of the corrupt entries seen since it was
+ *   last read.
  * - Shapes: head_dim d in {64, 128}; G = Hq / Hkv query heads per KV head (1..16); query head h
  *   reads KV head h / G.
  */
@@ -41,11 +47,13 @@ typedef enum {
   VC_EHIP = -3,         /* a HIP runtime call failed */
   VC_EUNSUPPORTED = -4, /* valid but not implemented (e.g. head_dim 96) */
   VC_ENOMEM = -5,       /* the page allocator has too few free pages of the asked kind */
-  VC_EAGAIN = -6        /* the scheduler has no room for the request now; retry after advancing */
+  VC_EAGAIN = -6,       /* the scheduler has no room for the request now; retry after advancing */
+  VC_EDEVICE = -7       /* a kernel met a page-table entry outside [-1, num_blocks) (vc_check_device) */
 } vc_status;
 
 #define VC_BLOCK_TOKENS 16   /* tokens per KV page */
-#define VC_MAX_REQS 64       /* requests per attention launch */
+#define VC_MAX_REQS 1024     /* requests per attention launch */
+#define VC_MAX_BATCH 128     /* requests per cache-building or commit call */
 #define VC_MAX_ROWS 64       /* drafted rows per request */
 #define VC_KIVI_GROUP 32     /* KIVI quantisation group (tokens for keys, channels for values) */
 
@@ -89,7 +97,8 @@ typedef struct {
   int32_t max_pages;           /* row stride of page_table */
   int64_t num_blocks;          /* nb: physical blocks per layer */
   const int32_t* page_table;   /* (device) int32 [rows][max_pages]; -1 = no block.  A context
-                                  page whose entry is -1 or >= num_blocks contributes no keys;
+                                  page whose entry is -1 contributes no keys (one outside
+                                  [-1, num_blocks) neither, and is reported as VC_EDEVICE);
                                   in a KIVI pool a missing even page 2j also removes page 2j+1
                                   (the group's key parameters live in page 2j's block) */
   const void* k;               /* (device) see above */
@@ -123,14 +132,17 @@ typedef struct {
  *   blk_v  bf16 [batch][L][Hkv][max_rows/16][d][16]   and values (channel-major pages)
  *   out    fp32 [batch][L][max_rows][Hq][d]      attention output; only rows q0..q0+rows-1 of
  *          each request are written
- *   workspace: device scratch for split-context partial results, at least
- *          vc_attn_workspace_size() bytes for the same arguments; may be NULL when that is 0.
+ *   workspace: device scratch, at least vc_attn_workspace_size() bytes for the same arguments
+ *          (may be NULL when that is 0): the launch's request table when it has more than 64
+ *          requests (written by the call itself, on the stream, before the attention kernel),
+ *          then the split-context partial results.  Calls that overlap on one workspace race.
  * Attention (VeriCache review, §Prerequisites, attention equation): softmax(q k^T / sqrt(d)) v,
  * fp32 accumulation, bf16 inputs, softmax weights rounded to bf16 for the value product.
  * split_pages: context pages per split (multiple of 4), 0 = automatic.
  */
 
-/* Bytes of workspace an attention call with these requests needs (0 if no split). */
+/* Bytes of workspace an attention call with these requests needs (0 if it has at most 64
+ * requests and no context is split), or 0 for arguments the call would reject. */
 size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req* reqs /* host */,
                               int split_pages);
 
@@ -160,9 +172,11 @@ int vc_attn_mixed(const vc_shape* shape, int num_reqs, const vc_req* reqs /* hos
  *   draft_logits  fp32 [n_inst][max_x][vocab]     row j = draft step j
  *   verify_logits fp32 [n_inst][max_xv][vocab]    row j = verifier prediction for slot j
  * Outputs (device): draft_tok int32 [n_inst][max_x], verify_tok int32 [n_inst][max_xv] (argmax,
- * ties to the lowest id; unused rows -1); accept_len int32 [n_inst] = first j with
- * draft_tok != verify_tok, else x; next_tok int32 [n_inst] = verify_tok[accept_len] if that row
- * exists, else -1.  x and xv are device arrays (values are clamped to [0, max_x], [0, max_xv]).
+ * ties to the lowest id; unused rows -1); accept_len int32 [n_inst] = first j < min(x, xv) with
+ * draft_tok != verify_tok, else min(x, xv); next_tok int32 [n_inst] = verify_tok[accept_len] if
+ * that row exists (accept_len < xv), else -1.  A verifier with fewer rows than drafted slots
+ * (xv < x) thus ends the block at its last row, as in vc_accept_sampled.  x and xv are device
+ * arrays (values are clamped to [0, max_x], [0, max_xv]); max_xv may be below max_x.
  * Logits must be finite.
  */
 int vc_accept(int n_inst, int max_x, int max_xv, int vocab, const int32_t* x, const int32_t* xv,
@@ -219,7 +233,9 @@ int vc_logits(int rows, int width, int vocab, const float* o, int64_t ld_o, cons
               float* z, void* stream);
 
 /* ---- Building caches (untimed preparation; VeriCache review, §Compression Method Integration:
- *      compress() runs once, offline, before serving) ---- */
+ *      compress() runs once, offline, before serving).  Each call takes 1 .. VC_MAX_BATCH
+ *      requests (page-table rows 0 .. batch-1); a larger batch is built by calls over row ranges.
+ *      A destination page whose entry is -1 is not written. ---- */
 
 /*
  * Write one layer of a bf16 paged pool from a dense tensor.
@@ -280,8 +296,8 @@ typedef struct {
  * vc_page_row_extend).  If kept is not NULL (int32 [batch][L][Hkv][kept_stride], device), the
  * positions are also appended to each (slot, layer, head) kept list at kept_len .. (token drop:
  * newly committed tokens are always kept).  blk_k / blk_v as in the attention calls.
- * Errors (nothing launched): VC_EINVAL for a non-bf16 pool, counts outside [0, max_rows], or
- * kept_len + count > kept_stride.
+ * Errors (nothing launched): VC_EINVAL for more than VC_MAX_BATCH commits, a non-bf16 pool,
+ * counts outside [0, max_rows], or kept_len + count > kept_stride.
  */
 int vc_commit_rows(const vc_shape* shape, int num, const vc_commit* commits /* host */,
                    const void* blk_k, const void* blk_v, const vc_pool* pool, int32_t* kept,
@@ -362,11 +378,24 @@ int vc_sched_due(const void* sched, int32_t cap, int32_t* reload_ids, int32_t* n
 
 /*
  * Copy `bytes` from pinned host memory (allocated with hipHostMalloc or equivalent) to device
- * memory on `side_stream`, then record `event` (a hipEvent_t as void*, may be NULL) on it.
- * The caller makes its verify stream wait on the event.  Nothing is synchronised here.
+ * memory on `side_stream`, then record `event` (a hipEvent_t as void*, may be NULL) on it; the
+ * event is recorded for bytes == 0 too.  The caller makes its verify stream wait on the event.
+ * Nothing is synchronised here.
+ * Errors (nothing enqueued): VC_EINVAL for NULL pointers with bytes > 0, a source that is not
+ * pinned host memory (a pageable source would make the copy synchronous, so the staging would no
+ * longer overlap the draft steps), or a destination that is not device memory.
  */
 int vc_stage_kv(void* dst_device, const void* src_pinned_host, size_t bytes, void* side_stream,
                 void* event);
+
+/*
+ * Report the device-side checks of earlier calls on the current device.  Synchronises `stream`
+ * (a hipStream_t as void*, NULL = the null stream), reads the device error word and clears it.
+ * Returns VC_OK, or VC_EDEVICE with the page-table row, logical page and entry of one corrupt
+ * page-table entry in vc_last_error().  Work still running on other streams may report later.
+ * This is the one call of the library that waits for the device.
+ */
+int vc_check_device(void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* vc_last_error(void);

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -23,6 +24,30 @@ int fail(int code, const std::string& msg) {
 int hip_check(hipError_t e, const char* what) {
   if (e == hipSuccess) return VC_OK;
   return fail(VC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// The device error word: [flag, page-table row, logical page, entry].  Each device holds its own
+// copy of the array; its address is looked up once per device.
+static __device__ __attribute__((aligned(16))) int32_t g_error_word[4];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_word_mu;
+static int32_t* g_word_ptr[kMaxDevices];
+
+int32_t* device_error_word() {
+  int dev = 0;
+  if (hip_check(hipGetDevice(&dev), "hipGetDevice")) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(VC_EUNSUPPORTED, "device index beyond the library's table");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_word_mu);
+  if (!g_word_ptr[dev]) {
+    void* p = nullptr;
+    if (hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(g_error_word)), "hipGetSymbolAddress")) return nullptr;
+    g_word_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  return g_word_ptr[dev];
 }
 
 static int check_shape(const vc_shape* s) {
@@ -131,10 +156,10 @@ static int auto_chunk(const vc_shape* s, int nreq, const vc_req* reqs, int vwave
 }
 
 int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const vc_pool* pools,
-              int split_pages, AttnArgs* args, Plan* plan) {
+              int split_pages, AttnArgs* args, Plan* plan, std::vector<ReqDev>* table) {
   int rc = check_shape(s);
   if (rc) return rc;
-  if (nreq < 0 || nreq > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 64]");
+  if (nreq < 0 || nreq > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 1024]");
   if (nreq > 0 && !reqs) return fail(VC_EINVAL, "reqs is NULL");
   if (npools < 1 || npools > kMaxPools) return fail(VC_EINVAL, "num_pools must be in [1, 4]");
   if (split_pages < 0 || split_pages % 4) return fail(VC_EINVAL, "split_pages must be a multiple of 4");
@@ -145,8 +170,9 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   std::vector<char> pool_used(npools, 0);
   const int vwaves = plan_vwaves(G, nreq, reqs);
   const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs, vwaves);
-  int64_t items = 0, part = 0;
+  int64_t items = 0, part = 0, merge = 0;
   plan->any_split = 0;
+  table->assign(nreq, ReqDev{});
   for (int i = 0; i < nreq; ++i) {
     const vc_req& r = reqs[i];
     char buf[200];
@@ -183,7 +209,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
                p.max_pages);
       return fail(VC_EINVAL, buf);
     }
-    ReqDev& d = args->reqs[i];
+    ReqDev& d = (*table)[i];
     d.slot = r.slot;
     d.pool = r.pool;
     d.ctx_len = r.ctx_len;
@@ -196,15 +222,23 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
     d.nrg = (int32_t)row_groups(r, G, vwaves);
     d.item_base = (int32_t)items;
     items += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * d.nrg;
+    // merge work-groups are counted for every request (a request without splits owns none), so
+    // merge_base ascends and the merge kernel finds a work-group's request like an item's
+    d.merge_base = (int32_t)std::min<int64_t>(merge, INT32_MAX);
     if (d.nsplit > 1) {
       d.part_base = part;
       part += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * r.rows * G * (D + 4);
+      const int64_t rows = (int64_t)s->num_layers * s->num_kv_heads * r.rows * G;
+      const int rpg = merge_rows_per_group(D);
+      merge += (rows + rpg - 1) / rpg;
       plan->any_split = 1;
     } else {
       d.part_base = -1;
     }
   }
   if (items > (1LL << 30)) return fail(VC_EINVAL, "too many work items");
+  if (merge > (1LL << 30)) return fail(VC_EINVAL, "too many split rows");
+  for (int i = 0; i < std::min(nreq, kInlineReqs); ++i) args->reqs[i] = (*table)[i];
   args->L = s->num_layers;
   args->Hq = s->num_q_heads;
   args->Hkv = s->num_kv_heads;
@@ -218,6 +252,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   // a launch mixing drafting and verifying requests is a ragged batch: spread every request over
   // the XCDs (64-request batch: 0.91-0.92 ms against 0.94-0.95 with XCD ranges)
   args->xcd_ranges = is_mixed(nreq, reqs) ? 0 : 1;
+  args->nmerge = (int32_t)merge;
   plan->nitems = (int)items;
   plan->vwaves = vwaves;
   plan->part_floats = part;
@@ -230,22 +265,37 @@ static int attn_common(const vc_shape* s, int nreq, const vc_req* reqs, const vo
                        float* out, void* ws, size_t ws_bytes, int split_pages, void* stream) {
   AttnArgs args;
   Plan plan;
-  int rc = plan_attn(s, nreq, reqs, npools, pools, split_pages, &args, &plan);
+  std::vector<ReqDev> table;
+  int rc = plan_attn(s, nreq, reqs, npools, pools, split_pages, &args, &plan, &table);
   if (rc) return rc;
   if (nreq == 0 || plan.nitems == 0) return VC_OK;
   if (!q || !blk_k || !blk_v || !out) return fail(VC_EINVAL, "q, blk_k, blk_v and out must be set");
-  const size_t need = (size_t)plan.part_floats * sizeof(float);
+  // workspace: [request table (more than kInlineReqs requests)][split partials]
+  const size_t tbytes = req_table_bytes(nreq);
+  const size_t need = tbytes + (size_t)plan.part_floats * sizeof(float);
   if (need > 0 && (!ws || ws_bytes < need)) {
     char buf[160];
     snprintf(buf, sizeof buf, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
     return fail(VC_ENOSPACE, buf);
   }
+  if (need > 0 && reinterpret_cast<uintptr_t>(ws) % 16)
+    return fail(VC_EINVAL, "workspace must be 16-byte aligned");
+  args.err = device_error_word();
+  if (!args.err) return VC_EHIP;
   args.q = static_cast<const uint16_t*>(q);
   args.blk_k = static_cast<const uint16_t*>(blk_k);
   args.blk_v = static_cast<const uint16_t*>(blk_v);
   args.out = out;
-  args.part = static_cast<float*>(ws);
-  return launch_attn(args, plan, s->head_dim, static_cast<hipStream_t>(stream));
+  args.part = need > tbytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + tbytes) : nullptr;
+  args.reqs_dev = nullptr;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tbytes) {
+    ReqDev* dtab = static_cast<ReqDev*>(ws);
+    rc = upload_req_table(table, dtab, st);
+    if (rc) return rc;
+    args.reqs_dev = dtab;
+  }
+  return launch_attn(args, plan, s->head_dim, st);
 }
 
 }  // namespace vc
@@ -256,13 +306,15 @@ extern "C" {
 
 const char* vc_last_error(void) { return g_last_error.c_str(); }
 
-const char* vc_version(void) { return "vc 0.1 gfx950"; }
+const char* vc_version(void) { return "vc 0.2 gfx950"; }
 
 size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req* reqs,
                               int split_pages) {
   // pools are not needed for sizing: validate with a permissive dummy pool per index
   if (check_shape(shape)) return 0;
   if (num_reqs <= 0 || num_reqs > VC_MAX_REQS || !reqs) return 0;
+  for (int i = 0; i < num_reqs; ++i)
+    if (reqs[i].ctx_len < 0 || reqs[i].rows < 1 || reqs[i].rows > VC_MAX_ROWS) return 0;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int chunk =
       split_pages > 0 ? split_pages : auto_chunk(shape, num_reqs, reqs, plan_vwaves(G, num_reqs, reqs));
@@ -277,23 +329,22 @@ size_t vc_attn_workspace_size(const vc_shape* shape, int num_reqs, const vc_req*
       floats += (size_t)shape->num_layers * shape->num_kv_heads * nsplit * reqs[i].rows * G *
                 (shape->head_dim + 4);
   }
-  return floats * sizeof(float);
+  return req_table_bytes(num_reqs) + floats * sizeof(float);
 }
 
 int vc_verify_attn(const vc_shape* shape, int num_reqs, const vc_req* reqs, const void* q,
                    const void* blk_k, const void* blk_v, const vc_pool* full, float* out,
                    void* workspace, size_t workspace_bytes, int split_pages, void* stream) {
   set_error("");
-  if (num_reqs < 0 || num_reqs > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 64]");
+  if (num_reqs < 0 || num_reqs > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 1024]");
   if (num_reqs > 0 && !reqs) return fail(VC_EINVAL, "reqs is NULL");
   if (!full) return fail(VC_EINVAL, "full pool is NULL");
-  vc_req rr[VC_MAX_REQS];
-  for (int i = 0; i < num_reqs; ++i) {
-    rr[i] = reqs[i];
-    rr[i].pool = 0;
-    rr[i].kind = VC_VERIFY;
+  std::vector<vc_req> rr(reqs, reqs + num_reqs);
+  for (vc_req& r : rr) {
+    r.pool = 0;
+    r.kind = VC_VERIFY;
   }
-  return attn_common(shape, num_reqs, rr, q, blk_k, blk_v, 1, full, out, workspace,
+  return attn_common(shape, num_reqs, rr.data(), q, blk_k, blk_v, 1, full, out, workspace,
                      workspace_bytes, split_pages, stream);
 }
 
@@ -301,16 +352,15 @@ int vc_draft_attn(const vc_shape* shape, int num_reqs, const vc_req* reqs, const
                   const void* blk_k, const void* blk_v, const vc_pool* comp, float* out,
                   void* workspace, size_t workspace_bytes, int split_pages, void* stream) {
   set_error("");
-  if (num_reqs < 0 || num_reqs > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 64]");
+  if (num_reqs < 0 || num_reqs > VC_MAX_REQS) return fail(VC_EINVAL, "num_reqs must be in [0, 1024]");
   if (num_reqs > 0 && !reqs) return fail(VC_EINVAL, "reqs is NULL");
   if (!comp) return fail(VC_EINVAL, "compressed pool is NULL");
-  vc_req rr[VC_MAX_REQS];
-  for (int i = 0; i < num_reqs; ++i) {
-    rr[i] = reqs[i];
-    rr[i].pool = 0;
-    rr[i].kind = VC_DRAFT;
+  std::vector<vc_req> rr(reqs, reqs + num_reqs);
+  for (vc_req& r : rr) {
+    r.pool = 0;
+    r.kind = VC_DRAFT;
   }
-  return attn_common(shape, num_reqs, rr, q, blk_k, blk_v, 1, comp, out, workspace,
+  return attn_common(shape, num_reqs, rr.data(), q, blk_k, blk_v, 1, comp, out, workspace,
                      workspace_bytes, split_pages, stream);
 }
 
@@ -324,17 +374,55 @@ int vc_attn_mixed(const vc_shape* shape, int num_reqs, const vc_req* reqs, const
                      workspace_bytes, split_pages, stream);
 }
 
+// Kind of memory `p` points into: hipMemoryTypeHost (pinned host), hipMemoryTypeDevice, ..., or
+// -1 for memory HIP does not know (pageable host memory; depending on the runtime version the
+// query fails for it, and the error it leaves is cleared here).
+static int memory_kind(const void* p) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof attr);
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return (int)attr.type;
+}
+
 int vc_stage_kv(void* dst_device, const void* src_pinned_host, size_t bytes, void* side_stream,
                 void* event) {
   set_error("");
-  if (bytes == 0) return VC_OK;
-  if (!dst_device || !src_pinned_host) return fail(VC_EINVAL, "dst and src must be set");
   hipStream_t st = static_cast<hipStream_t>(side_stream);
-  int rc = hip_check(hipMemcpyAsync(dst_device, src_pinned_host, bytes, hipMemcpyHostToDevice, st),
-                     "hipMemcpyAsync");
+  if (bytes > 0) {
+    if (!dst_device || !src_pinned_host) return fail(VC_EINVAL, "dst and src must be set");
+    if (memory_kind(src_pinned_host) != (int)hipMemoryTypeHost)
+      return fail(VC_EINVAL, "the staging source is not pinned host memory (hipHostMalloc): a pageable "
+                             "source would make the copy synchronous");
+    if (memory_kind(dst_device) != (int)hipMemoryTypeDevice)
+      return fail(VC_EINVAL, "the staging destination is not device memory");
+    const int rc = hip_check(hipMemcpyAsync(dst_device, src_pinned_host, bytes, hipMemcpyHostToDevice, st),
+                             "hipMemcpyAsync");
+    if (rc) return rc;
+  }
+  return event ? hip_check(hipEventRecord(static_cast<hipEvent_t>(event), st), "hipEventRecord") : VC_OK;
+}
+
+int vc_check_device(void* stream) {
+  set_error("");
+  int32_t* w = device_error_word();
+  if (!w) return VC_EHIP;
+  int rc = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
   if (rc) return rc;
-  if (event) rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(event), st), "hipEventRecord");
-  return rc;
+  int32_t h[4] = {0, 0, 0, 0};
+  rc = hip_check(hipMemcpy(h, w, sizeof h, hipMemcpyDeviceToHost), "hipMemcpy (error word)");
+  if (rc) return rc;
+  if (!h[0]) return VC_OK;
+  const int32_t zero[4] = {0, 0, 0, 0};
+  rc = hip_check(hipMemcpy(w, zero, sizeof zero, hipMemcpyHostToDevice), "hipMemcpy (error word)");
+  if (rc) return rc;
+  char buf[200];
+  snprintf(buf, sizeof buf,
+           "a kernel read page-table row %d, logical page %d: block id %d is outside [-1, num_blocks) "
+           "(the page was treated as absent)", h[1], h[2], h[3]);
+  return fail(VC_EDEVICE, buf);
 }
 
 }  // extern "C"

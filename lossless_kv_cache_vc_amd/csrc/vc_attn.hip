@@ -23,6 +23,7 @@
 // workspace and a merge kernel combines them with log-sum-exp weights.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "vc_internal.h"
@@ -615,7 +616,10 @@ __device__ __forceinline__ void verify_begin(const AttnArgs& a, const ItemCtx& i
       const int phys = pt[i];
       const bool ok = phys >= 0 && phys < pl.nblk;
       units[i] = ok ? (int32_t)(vs.dummy_unit + (int64_t)phys * a.Hkv) : -1;
-      if (!ok) atomicMin(first_bad, i);
+      if (!ok) {
+        atomicMin(first_bad, i);
+        if (phys != -1) report_bad_page(a.err, rq.page_row, it.p_lo + i, phys);
+      }
     }
   }
   wait_vmem<0>();
@@ -1132,7 +1136,9 @@ __device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
     for (int i = tid; i < it.nctx; i += 64 * NW) {
       const int phys = pt[i];
-      ids[i] = (phys < 0 || phys >= pl.nblk) ? -1 : phys;
+      const bool ok = phys >= 0 && phys < pl.nblk;
+      ids[i] = ok ? phys : -1;
+      if (!ok && phys != -1) report_bad_page(a.err, rq.page_row, it.p_lo + i, phys);
     }
   }
   wait_vmem<0>();
@@ -1553,7 +1559,10 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       const int phys = pt[i];
       const bool ok = phys >= 0 && phys < pl.nblk;
       ids[i] = ok ? phys : -1;
-      if (!ok) atomicMin(first_bad, i);
+      if (!ok) {
+        atomicMin(first_bad, i);
+        if (phys != -1) report_bad_page(a.err, rq.page_row, it.p_lo + i, phys);
+      }
     }
   }
   wait_vmem<0>();
@@ -1755,15 +1764,54 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 // share K/V (row groups of one unit) run on the same L2; without, work-group b takes item b, so
 // every request of a ragged batch is spread over all XCDs instead of each XCD holding a range of
 // requests of unequal cost.
+// Request of a work item (or merge work-group) in a device request table: the last entry whose
+// base (item_base, or merge_base when MERGE) is at most `key`.  The bases ascend, and entry 0's
+// is 0.  The wave narrows the range 64-fold per step (1024 requests: two loads per lane), and
+// the result is wave-uniform.
+template <bool MERGE>
+__device__ __forceinline__ int find_req_dev(const ReqDev* t, int n, int key) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, cnt = n;
+  while (cnt > 1) {
+    const int step = (cnt + 63) >> 6;
+    const bool in = lane * step < cnt;
+    const int idx = lo + (in ? lane * step : 0);
+    const int base = MERGE ? t[idx].merge_base : t[idx].item_base;
+    const uint64_t m = __ballot(in && base <= key);
+    const int j = 63 - __builtin_clzll(m | 1ull);  // lane 0 always qualifies
+    lo += j * step;
+    cnt = min(step, cnt - j * step);
+  }
+  return __builtin_amdgcn_readfirstlane(lo);
+}
+
+// Entry r of a device request table as wave-uniform values: the loads are vector loads (the
+// compiler cannot prove the table unchanged by the kernel's own stores, so it does not use the
+// scalar cache), and reading every word back through readfirstlane keeps the request's fields in
+// scalar registers, as they are when they come from the kernel arguments.
+__device__ __forceinline__ ReqDev uniform_req(const ReqDev* t, int r) {
+  constexpr int W = sizeof(ReqDev) / 4;
+  const int32_t* src = reinterpret_cast<const int32_t*>(t + r);
+  int32_t w[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) w[i] = __builtin_amdgcn_readfirstlane(src[i]);
+  return __builtin_bit_cast(ReqDev, w);
+}
+
 __device__ __forceinline__ bool decode_item(const AttnArgs& a, ItemCtx* it, int* rg) {
   const int b = blockIdx.x;
   const int per = a.nitems_pad >> 3;
   const int item = a.xcd_ranges ? (b & 7) * per + (b >> 3) : b;
   if (item >= a.nitems) return false;
-  int r = 0;
-  for (int i = 1; i < a.nreq; ++i)
-    if (item >= a.reqs[i].item_base) r = i;
-  const ReqDev& rq = a.reqs[r];
+  ReqDev rq;
+  if (a.reqs_dev) {
+    rq = uniform_req(a.reqs_dev, find_req_dev<false>(a.reqs_dev, a.nreq, item));
+  } else {
+    int r = 0;
+    for (int i = 1; i < a.nreq; ++i)
+      if (item >= a.reqs[i].item_base) r = i;
+    rq = a.reqs[r];
+  }
   int local = item - rq.item_base;
   *rg = local % rq.nrg;
   local /= rq.nrg;
@@ -1850,25 +1898,32 @@ __global__ __launch_bounds__(kVThreads) void mixed_kernel(const AttnArgs a) {
 // numbered over the (layer, kv head) units of the split requests in request order.  One pass
 // over the splits: the running maximum moves when a split's is larger (the sum and the output
 // are rescaled then).
+// Merge work-groups are dealt per request: request r owns work-groups merge_base[r] ..
+// merge_base[r + 1] - 1 (merge_base is the running count, so requests without splits own none).
+template <int D>
+constexpr int merge_rows_per_group() {
+  return 256 / (D / 4);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
   constexpr int LPR = D / 4;
-  constexpr int RPB = 256 / LPR;
-  int64_t rg = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int cq = threadIdx.x % LPR;
-  int r = -1;
-  for (int i = 0; i < a.nreq; ++i) {
-    if (a.reqs[i].nsplit <= 1) continue;
-    const int64_t cnt = (int64_t)a.L * a.Hkv * a.reqs[i].rows * a.G;
-    if (rg < cnt) {
-      r = i;
-      break;
-    }
-    rg -= cnt;
+  constexpr int RPB = merge_rows_per_group<D>();
+  const int b = blockIdx.x;
+  ReqDev rq;
+  if (a.reqs_dev) {
+    rq = uniform_req(a.reqs_dev, find_req_dev<true>(a.reqs_dev, a.nreq, b));
+  } else {
+    int r = 0;
+    for (int i = 1; i < a.nreq; ++i)
+      if (b >= a.reqs[i].merge_base) r = i;
+    rq = a.reqs[r];
   }
-  if (r < 0) return;
-  const ReqDev& rq = a.reqs[r];
+  if (rq.nsplit <= 1) return;
   const int rows_total = rq.rows * a.G;
+  const int64_t rg = (int64_t)(b - rq.merge_base) * RPB + threadIdx.x / LPR;
+  if (rg >= (int64_t)a.L * a.Hkv * rows_total) return;
+  const int cq = threadIdx.x % LPR;
   const int64_t unit = rg / rows_total;  // l * Hkv + g
   const int row = (int)(rg % rows_total);
   const int g = (int)(unit % a.Hkv), l = (int)(unit / a.Hkv);
@@ -1929,17 +1984,52 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
   }
   int rc = hip_check(hipGetLastError(), "attention launch");
   if (rc) return rc;
-  if (plan.any_split) {
-    int64_t nmerge = 0;
-    for (int i = 0; i < args.nreq; ++i)
-      if (args.reqs[i].nsplit > 1) nmerge += (int64_t)args.L * args.Hkv * args.reqs[i].rows * args.G;
-    const int rpb = 256 / (head_dim / 4);  // rows per merge work-group
-    const dim3 mgrid((unsigned)((nmerge + rpb - 1) / rpb));
+  if (plan.any_split && args.nmerge > 0) {
+    const dim3 mgrid((unsigned)args.nmerge);
     if (head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, args);
     else hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, args);
     rc = hip_check(hipGetLastError(), "merge launch");
   }
   return rc;
+}
+
+int merge_rows_per_group(int head_dim) {
+  return head_dim == 128 ? merge_rows_per_group<128>() : merge_rows_per_group<64>();
+}
+
+// ------------------------------------------------------------------ request table upload
+// A launch with more requests than the kernel arguments hold reads its request table from device
+// memory.  The table is written there by kernels whose own arguments carry the entries (up to
+// kUploadReqs per launch), so the copy is ordered on the stream like the attention launch and
+// needs no host staging buffer.
+namespace {
+constexpr int kUploadReqs = 64;
+struct ReqUpload {
+  ReqDev* dst;
+  int32_t n;
+  ReqDev reqs[kUploadReqs];
+};
+static_assert(sizeof(ReqUpload) <= 4096, "kernel arguments must fit 4 KiB");
+
+__global__ __launch_bounds__(256) void upload_reqs_kernel(const ReqUpload u) {
+  constexpr int W = sizeof(ReqDev) / 4;  // 32-bit words per entry
+  const int32_t* src = reinterpret_cast<const int32_t*>(u.reqs);
+  int32_t* dst = reinterpret_cast<int32_t*>(u.dst);
+  for (int i = threadIdx.x; i < u.n * W; i += blockDim.x) dst[i] = src[i];
+}
+}  // namespace
+
+int upload_req_table(const std::vector<ReqDev>& table, ReqDev* dst, hipStream_t stream) {
+  for (size_t i0 = 0; i0 < table.size(); i0 += kUploadReqs) {
+    ReqUpload u;
+    u.dst = dst + i0;
+    u.n = (int32_t)std::min<size_t>(kUploadReqs, table.size() - i0);
+    for (int j = 0; j < u.n; ++j) u.reqs[j] = table[i0 + j];
+    hipLaunchKernelGGL(upload_reqs_kernel, dim3(1), dim3(256), 0, stream, u);
+    const int rc = hip_check(hipGetLastError(), "request table upload");
+    if (rc) return rc;
+  }
+  return VC_OK;
 }
 
 }  // namespace vc

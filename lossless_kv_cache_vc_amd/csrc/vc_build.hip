@@ -13,8 +13,6 @@ namespace vc {
 
 namespace {
 
-constexpr int kMaxBatch = VC_MAX_REQS;
-
 struct BatchInfo {
   int32_t n;                 // requests
   int32_t lens[kMaxBatch];   // tokens per request
@@ -34,13 +32,17 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 // job = (request, page, kv head); src bf16 [batch][Hkv][src_rows][d]
 template <int D>
 __global__ __launch_bounds__(256) void pack_kernel(BatchInfo bi, int Hkv, int layer, const uint16_t* src,
-                                                   int64_t src_rows, PoolDev pool, int which) {
+                                                   int64_t src_rows, PoolDev pool, int which, int32_t* err) {
   const int job = blockIdx.x;
   const int r = find_req(bi, job);
   int local = job - bi.base[r];
   const int g = local % Hkv, p = local / Hkv;
   const int len = bi.lens[r];
   const int phys = pool.page_table[(int64_t)r * pool.max_pages + p];
+  if (phys < 0 || phys >= pool.nblk) {  // an unmapped page is not written; a corrupt id is reported
+    if (phys != -1) report_bad_page(err, r, p, phys);
+    return;
+  }
   const int64_t unit = ((int64_t)layer * pool.nblk + phys) * Hkv + g;
   const uint16_t* s = src + (((int64_t)r * Hkv + g) * src_rows) * D;
   if (which == 0) {
@@ -187,11 +189,23 @@ struct CompInfo {
   int32_t base[kMaxBatch + 1];  // prefix of jobs
 };
 
-// a source position maps to a block of the source pool (bad table entries read as zeros)
-__device__ __forceinline__ bool src_ok(const PoolDev& s, int r, int pos) {
+// a source position maps to a block of the source pool (missing pages read as zeros; a corrupt
+// table entry is reported and read as zeros too)
+__device__ __forceinline__ bool src_ok(const PoolDev& s, int r, int pos, int32_t* err) {
   if (pos < 0 || pos >= s.max_pages * kBlock) return false;
   const int phys = s.page_table[(int64_t)r * s.max_pages + pos / kBlock];
-  return phys >= 0 && phys < s.nblk;
+  if (phys >= 0 && phys < s.nblk) return true;
+  if (phys != -1) report_bad_page(err, r, pos / kBlock, phys);
+  return false;
+}
+
+// a destination page of a compressed pool: its block id, or -1 when it is unmapped (not written)
+// or corrupt (reported, not written)
+__device__ __forceinline__ int dst_block(const PoolDev& d, int r, int page, int32_t* err) {
+  const int phys = d.page_table[(int64_t)r * d.max_pages + page];
+  if (phys >= 0 && phys < d.nblk) return phys;
+  if (phys != -1) report_bad_page(err, r, page, phys);
+  return -1;
 }
 
 // source token `pos` of (r, l, g) in a bf16 pool: key row / value element pointers
@@ -211,7 +225,8 @@ __device__ __forceinline__ const uint16_t* src_v_page(const PoolDev& s, int Hkv,
 // bf16 token drop: job = (r, l, g, destination page)
 template <int D>
 __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, int Hkv, PoolDev src,
-                                                          const int32_t* kept, int64_t kstride, PoolDev dst) {
+                                                          const int32_t* kept, int64_t kstride, PoolDev dst,
+                                                          int32_t* err) {
   const int job = blockIdx.x;
   int r = 0;
   for (int i = 1; i < ci.n; ++i)
@@ -224,8 +239,8 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, in
   const int g = local % Hkv, l = local / Hkv;
   const int T = ci.lens[r];
   const int32_t* kp = kept ? kept + ((int64_t)(r * L + l) * Hkv + g) * kstride : nullptr;
-  const int phys = dst.page_table[(int64_t)r * dst.max_pages + p];
-  if (phys < 0 || phys >= dst.nblk) return;  // unmapped destination page
+  const int phys = dst_block(dst, r, p, err);
+  if (phys < 0) return;  // unmapped (or corrupt) destination page
   const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
   uint8_t* dk = const_cast<uint8_t*>(dst.k) + unit * (kBlock * D * 2);
   uint16_t* dv = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.v) + unit * (kBlock * D * 2));
@@ -235,7 +250,7 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, in
     u32x4 v = {0, 0, 0, 0};
     if (j < T) {
       const int pos = kp ? kp[j] : j;
-      if (src_ok(src, r, pos)) v = ld16(src_k_row<D>(src, Hkv, r, l, g, pos) + 8 * cc);
+      if (src_ok(src, r, pos, err)) v = ld16(src_k_row<D>(src, Hkv, r, l, g, pos) + 8 * cc);
     }
     *reinterpret_cast<u32x4*>(dk + c * 16) = v;
   }
@@ -245,7 +260,7 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(CompInfo ci, int L, in
     uint16_t v = 0;
     if (j < T) {
       const int pos = kp ? kp[j] : j;
-      if (src_ok(src, r, pos)) v = src_v_page<D>(src, Hkv, r, l, g, pos)[dd * kBlock + pos % kBlock];
+      if (src_ok(src, r, pos, err)) v = src_v_page<D>(src, Hkv, r, l, g, pos)[dd * kBlock + pos % kBlock];
     }
     dv[e] = v;
   }
@@ -302,7 +317,8 @@ __device__ __forceinline__ int code_bitpos(int u, int bits) { return (u & 1) * 1
 // KIVI-style quantisation: job = (r, l, g, 32-token group j) of the stored sequence.
 template <int D>
 __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, PoolDev src,
-                                                   const int32_t* kept, int64_t kstride, PoolDev dst) {
+                                                   const int32_t* kept, int64_t kstride, PoolDev dst,
+                                                   int32_t* err) {
   __shared__ uint16_t xk[32][D];   // gathered bf16 keys of the group
   __shared__ uint16_t xv[32][D];
   __shared__ uint8_t ck[32][D];    // codes
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
     uint16_t kv = 0, vv = 0;
     if (t < cnt) {
       const int pos = kp ? kp[t0 + t] : t0 + t;
-      if (src_ok(src, r, pos)) {
+      if (src_ok(src, r, pos, err)) {
         kv = src_k_row<D>(src, Hkv, r, l, g, pos)[c];
         vv = src_v_page<D>(src, Hkv, r, l, g, pos)[c * kBlock + pos % kBlock];
       }
@@ -338,8 +354,8 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
   __syncthreads();
 
   const int p_even = 2 * j;
-  const int phys_e = dst.page_table[(int64_t)r * dst.max_pages + p_even];
-  if (phys_e < 0 || phys_e >= dst.nblk) return;  // unmapped destination: the group is skipped
+  const int phys_e = dst_block(dst, r, p_even, err);
+  if (phys_e < 0) return;  // unmapped (or corrupt) destination: the group is skipped
   const int64_t unit_e = ((int64_t)l * dst.nblk + phys_e) * Hkv + g;
   // keys: one channel per thread, group over the cnt tokens
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
@@ -372,8 +388,8 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
       for (int c = 32 * gq; c < 32 * gq + 32; ++c)
         cv[t][c] = (uint8_t)quant_code(bf16_to_f64(xv[t][c]), s16, z16, levels);
       const int page = (t0 + t) / kBlock, tt = (t0 + t) % kBlock;
-      const int phys = dst.page_table[(int64_t)r * dst.max_pages + page];
-      if (phys >= 0 && phys < dst.nblk) {
+      const int phys = dst_block(dst, r, page, err);
+      if (phys >= 0) {
         const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
         uint16_t* vsz = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(dst.vsz) + unit * (D / 32 * kBlock * 4));
         vsz[(gq * 2) * kBlock + tt] = s16;      // [group][scale plane][token]
@@ -389,8 +405,8 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
   for (int hp = 0; hp < 2; ++hp) {
     const int page = p_even + hp;
     if (16 * hp >= cnt) break;
-    const int phys = dst.page_table[(int64_t)r * dst.max_pages + page];
-    if (phys < 0 || phys >= dst.nblk) continue;
+    const int phys = dst_block(dst, r, page, err);
+    if (phys < 0) continue;
     const int64_t unit = ((int64_t)l * dst.nblk + phys) * Hkv + g;
     uint32_t* kw = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.k) + unit * (2 * D * bits));
     uint32_t* vw = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.v) + unit * (2 * D * bits));
@@ -412,7 +428,7 @@ __global__ __launch_bounds__(256) void kivi_kernel(CompInfo ci, int L, int Hkv, 
 }
 
 int fill_batch(int batch, const int32_t* lens, BatchInfo* bi, int per_page_jobs) {
-  if (batch < 1 || batch > kMaxBatch) return fail(VC_EINVAL, "batch must be in [1, 64]");
+  if (batch < 1 || batch > kMaxBatch) return fail(VC_EINVAL, "batch must be in [1, 128]");
   if (!lens) return fail(VC_EINVAL, "lens is NULL");
   memset(bi, 0, sizeof(*bi));
   bi->n = batch;
@@ -463,13 +479,15 @@ int vc_pack_bf16(const vc_shape* shape, int batch, const int32_t* lens, int laye
   if (bi.base[batch] == 0) return VC_OK;
   PoolDev pd = {static_cast<const uint8_t*>(pool->k), static_cast<const uint8_t*>(pool->v), nullptr,
                 nullptr, pool->page_table, pool->num_blocks, pool->max_pages, 16};
+  int32_t* err = device_error_word();
+  if (!err) return VC_EHIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (shape->head_dim == 128)
     hipLaunchKernelGGL(pack_kernel<128>, dim3(bi.base[batch]), dim3(256), 0, st, bi, shape->num_kv_heads,
-                       layer, static_cast<const uint16_t*>(src), src_rows, pd, which);
+                       layer, static_cast<const uint16_t*>(src), src_rows, pd, which, err);
   else
     hipLaunchKernelGGL(pack_kernel<64>, dim3(bi.base[batch]), dim3(256), 0, st, bi, shape->num_kv_heads,
-                       layer, static_cast<const uint16_t*>(src), src_rows, pd, which);
+                       layer, static_cast<const uint16_t*>(src), src_rows, pd, which, err);
   return hip_check(hipGetLastError(), "pack launch");
 }
 
@@ -479,7 +497,7 @@ int vc_select_kept(const vc_shape* shape, int batch, const int32_t* lens, const 
   set_error("");
   int rc = shape_ok(shape);
   if (rc) return rc;
-  if (batch < 1 || batch > kMaxBatch) return fail(VC_EINVAL, "batch must be in [1, 64]");
+  if (batch < 1 || batch > kMaxBatch) return fail(VC_EINVAL, "batch must be in [1, 128]");
   if (!lens || !recent || !top || !scores || !kept) return fail(VC_EINVAL, "NULL argument");
   SelectInfo si;
   memset(&si, 0, sizeof si);
@@ -537,14 +555,16 @@ int vc_compress_tail(const vc_shape* shape, int batch, const int32_t* from_lens,
   PoolDev d = {static_cast<const uint8_t*>(dst->k), static_cast<const uint8_t*>(dst->v),
                static_cast<const uint8_t*>(dst->k_sz), static_cast<const uint8_t*>(dst->v_sz),
                dst->page_table, dst->num_blocks, dst->max_pages, dst->bits};
+  int32_t* err = device_error_word();
+  if (!err) return VC_EHIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool d128 = shape->head_dim == 128;
   if (dst->bits == 16) {
-    if (d128) hipLaunchKernelGGL(gather_bf16_kernel<128>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d);
-    else hipLaunchKernelGGL(gather_bf16_kernel<64>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d);
+    if (d128) hipLaunchKernelGGL(gather_bf16_kernel<128>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d, err);
+    else hipLaunchKernelGGL(gather_bf16_kernel<64>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d, err);
   } else {
-    if (d128) hipLaunchKernelGGL(kivi_kernel<128>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d);
-    else hipLaunchKernelGGL(kivi_kernel<64>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d);
+    if (d128) hipLaunchKernelGGL(kivi_kernel<128>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d, err);
+    else hipLaunchKernelGGL(kivi_kernel<64>, dim3(acc), dim3(256), 0, st, ci, L, Hkv, s, kept, kept_stride, d, err);
   }
   return hip_check(hipGetLastError(), "compress launch");
 }

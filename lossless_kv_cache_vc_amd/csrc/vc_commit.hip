@@ -11,7 +11,7 @@ namespace vc {
 
 namespace {
 
-constexpr int kMaxCommits = VC_MAX_REQS;
+constexpr int kMaxCommits = VC_MAX_BATCH;
 
 struct CommitInfo {
   int32_t n;
@@ -22,7 +22,8 @@ struct CommitInfo {
 template <int D>
 __global__ __launch_bounds__(256) void commit_rows_kernel(CommitInfo ci, int L, int Hkv, int xmax,
                                                           const uint16_t* blk_k, const uint16_t* blk_v,
-                                                          PoolDev pool, int32_t* kept, int64_t kstride) {
+                                                          PoolDev pool, int32_t* kept, int64_t kstride,
+                                                          int32_t* err) {
   const int job = blockIdx.x;
   const int g = job % Hkv, l = (job / Hkv) % L, i = job / (Hkv * L);
   const vc_commit cm = ci.c[i];
@@ -34,7 +35,10 @@ __global__ __launch_bounds__(256) void commit_rows_kernel(CommitInfo ci, int L, 
     const uint16_t* src = blk_k + (bunit0 + j / kBlock) * (kBlock * D) + (j % kBlock) * D + 8 * c8;
     const int pos = cm.pos + j;
     const int phys = pool.page_table[(int64_t)cm.page_row * pool.max_pages + pos / kBlock];
-    if (phys < 0 || phys >= pool.nblk) continue;  // an unmapped page: nothing to write
+    if (phys < 0 || phys >= pool.nblk) {  // an unmapped page: nothing to write; a corrupt id is reported
+      if (phys != -1) report_bad_page(err, cm.page_row, pos / kBlock, phys);
+      continue;
+    }
     const int64_t unit = ((int64_t)l * pool.nblk + phys) * Hkv + g;
     uint16_t* dst = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(pool.k) + unit * (kBlock * D * 2)) +
                     (pos % kBlock) * D + 8 * c8;
@@ -46,7 +50,10 @@ __global__ __launch_bounds__(256) void commit_rows_kernel(CommitInfo ci, int L, 
     const uint16_t v = blk_v[(bunit0 + j / kBlock) * (kBlock * D) + dd * kBlock + j % kBlock];
     const int pos = cm.pos + j;
     const int phys = pool.page_table[(int64_t)cm.page_row * pool.max_pages + pos / kBlock];
-    if (phys < 0 || phys >= pool.nblk) continue;
+    if (phys < 0 || phys >= pool.nblk) {
+      if (phys != -1) report_bad_page(err, cm.page_row, pos / kBlock, phys);
+      continue;
+    }
     const int64_t unit = ((int64_t)l * pool.nblk + phys) * Hkv + g;
     reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(pool.v) + unit * (kBlock * D * 2))[dd * kBlock + pos % kBlock] = v;
   }
@@ -72,7 +79,7 @@ int vc_commit_rows(const vc_shape* shape, int num, const vc_commit* commits, con
   if (L < 1 || Hkv < 1) return fail(VC_EINVAL, "bad shape");
   if (d != 64 && d != 128) return fail(VC_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (xmax < kBlock || xmax > VC_MAX_ROWS || xmax % kBlock) return fail(VC_EINVAL, "max_rows must be 16, 32, 48 or 64");
-  if (num < 0 || num > kMaxCommits) return fail(VC_EINVAL, "num must be in [0, 64]");
+  if (num < 0 || num > kMaxCommits) return fail(VC_EINVAL, "num must be in [0, 128]");
   if (num == 0) return VC_OK;
   if (!commits || !blk_k || !blk_v || !pool) return fail(VC_EINVAL, "NULL argument");
   if (pool->bits != 16 || !pool->k || !pool->v || !pool->page_table) return fail(VC_EINVAL, "commit writes a bf16 pool");
@@ -90,14 +97,16 @@ int vc_commit_rows(const vc_shape* shape, int num, const vc_commit* commits, con
   }
   PoolDev p = {static_cast<const uint8_t*>(pool->k), static_cast<const uint8_t*>(pool->v), nullptr, nullptr,
                pool->page_table, pool->num_blocks, pool->max_pages, 16};
+  int32_t* err = device_error_word();
+  if (!err) return VC_EHIP;
   const dim3 grid(num * L * Hkv);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* bk = static_cast<const uint16_t*>(blk_k);
   const uint16_t* bv = static_cast<const uint16_t*>(blk_v);
   if (d == 128)
-    hipLaunchKernelGGL(commit_rows_kernel<128>, grid, dim3(256), 0, st, ci, L, Hkv, xmax, bk, bv, p, kept, kept_stride);
+    hipLaunchKernelGGL(commit_rows_kernel<128>, grid, dim3(256), 0, st, ci, L, Hkv, xmax, bk, bv, p, kept, kept_stride, err);
   else
-    hipLaunchKernelGGL(commit_rows_kernel<64>, grid, dim3(256), 0, st, ci, L, Hkv, xmax, bk, bv, p, kept, kept_stride);
+    hipLaunchKernelGGL(commit_rows_kernel<64>, grid, dim3(256), 0, st, ci, L, Hkv, xmax, bk, bv, p, kept, kept_stride, err);
   return hip_check(hipGetLastError(), "commit launch");
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string>
+#include <vector>
 
 #include "../../include/vc.h"
 
@@ -25,7 +26,27 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = VC_BLOCK_TOKENS;
-constexpr int kMaxReqs = VC_MAX_REQS;
+constexpr int kMaxReqs = VC_MAX_REQS;    // requests of one attention launch
+constexpr int kInlineReqs = 64;          // of those, carried in the kernel argument block
+constexpr int kMaxBatch = VC_MAX_BATCH;  // requests of one cache-building or commit call
+
+// ---------------------------------------------------------------- device error word
+// One word block per device (a file-scope __device__ array of the library): a kernel that reads a
+// page-table entry outside [-1, num_blocks) stores [1, page-table row, logical page, entry] into
+// it with ordinary vector stores and treats the page as missing.  vc_check_device() reads and
+// clears it.  Returns the current device's copy (NULL and a recorded error if HIP fails).
+int32_t* device_error_word();
+
+// Record a bad page-table entry (any lane may call it; concurrent writers store the same kind of
+// report, and one of them is kept).
+__device__ __forceinline__ void report_bad_page(int32_t* err, int row, int page, int id) {
+  if (err) {
+    err[1] = row;
+    err[2] = page;
+    err[3] = id;
+    err[0] = 1;
+  }
+}
 
 // Pool descriptor as the kernels see it (passed by value in kernel arguments).
 struct PoolDev {
@@ -39,15 +60,18 @@ struct PoolDev {
   int32_t bits;
 };
 
-// Per-request launch plan (host computed, passed by value).
+// Per-request launch plan (host computed; in the kernel arguments for up to kInlineReqs
+// requests, else in a device table at the head of the workspace).
 struct ReqDev {
   int32_t slot, pool, ctx_len, page_row, q0, rows, kind;
   int32_t item_base;    // first work item of this request
   int32_t nsplit;       // context splits per (layer, kv head)
   int32_t nrg;          // row groups per (layer, kv head, split) (verify); 1 for draft
   int32_t chunk_pages;  // context pages per split
+  int32_t merge_base;   // first merge row of this request (split requests; -1 otherwise)
   int64_t part_base;    // float offset of this request's partials in the workspace (-1: none)
 };
+static_assert(sizeof(ReqDev) == 56, "request table entry");
 
 constexpr int kMaxPools = 4;
 
@@ -64,7 +88,10 @@ struct AttnArgs {
                      // waves, one per 32 rows, over groups of 32 * vwaves rows (wide verify)
   int32_t xcd_ranges;  // 1: each XCD takes a contiguous range of items (row groups of a unit
                        // share an L2); 0: work-group b takes item b (ragged batches)
-  ReqDev reqs[kMaxReqs];
+  int32_t nmerge;      // merge rows of the split requests
+  int32_t* err;        // device error word (bad page-table entries)
+  const ReqDev* reqs_dev;  // request table in device memory when nreq > kInlineReqs, else NULL
+  ReqDev reqs[kInlineReqs];
 };
 
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit 4 KiB");
@@ -78,9 +105,22 @@ struct Plan {
   int head_dim = 0;
 };
 int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const vc_pool* pools,
-              int split_pages, AttnArgs* args, Plan* plan);
+              int split_pages, AttnArgs* args, Plan* plan, std::vector<ReqDev>* table);
+
+// Bytes at the head of the workspace that hold the request table of an nreq-request launch
+// (0 when the table fits the kernel arguments), rounded up to 256.
+inline size_t req_table_bytes(int nreq) {
+  return nreq > kInlineReqs ? ((size_t)nreq * sizeof(ReqDev) + 255) / 256 * 256 : 0;
+}
+
+// Enqueue the copy of a request table into device memory at `dst` (small kernels whose arguments
+// carry the entries, so nothing is staged on the host and nothing synchronises).
+int upload_req_table(const std::vector<ReqDev>& table, ReqDev* dst, hipStream_t stream);
 
 int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_t stream);
+
+// Rows of split partials one merge work-group combines (256 threads, d / 4 per row).
+int merge_rows_per_group(int head_dim);
 
 // Largest wide-verify work-group: 12 waves (3 per SIMD), 384 query rows.
 constexpr int kWideMaxWaves = 12;

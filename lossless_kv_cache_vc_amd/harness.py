@@ -115,8 +115,32 @@ class Workload:
 
     @staticmethod
     def _row(pool: vc.PagedPool, r: int) -> vc.PagedPool:
-        return vc.PagedPool(pool.bits, pool.page_table[r:r + 1], pool.k, pool.v, pool.num_blocks,
+        return Workload._rows(pool, r, r + 1)
+
+    @staticmethod
+    def _rows(pool: vc.PagedPool, r0: int, r1: int) -> vc.PagedPool:
+        """The pool seen through page-table rows r0 .. r1 - 1 (they become rows 0 ..)."""
+        return vc.PagedPool(pool.bits, pool.page_table[r0:r1], pool.k, pool.v, pool.num_blocks,
                             pool.k_sz, pool.v_sz)
+
+    @staticmethod
+    def _chunks(n: int):
+        """Request ranges of at most vc.MAX_BATCH for the cache-building and commit calls."""
+        return [(r0, min(n, r0 + vc.MAX_BATCH)) for r0 in range(0, n, vc.MAX_BATCH)]
+
+    def _compress(self, lens, src: vc.PagedPool, kept, dst: vc.PagedPool, from_lens=None):
+        """vc_compress / vc_compress_tail over the batch, in request ranges the calls accept."""
+        stride = kept.shape[-1] if kept is not None else 0
+        for r0, r1 in self._chunks(len(lens)):
+            if not any(lens[r0:r1]):
+                continue
+            kk = kept[r0:r1] if kept is not None else None
+            if from_lens is None:
+                vc.compress(self.shape, lens[r0:r1], self._rows(src, r0, r1), kk, stride,
+                            self._rows(dst, r0, r1))
+            else:
+                vc.compress_tail(self.shape, from_lens[r0:r1], lens[r0:r1], self._rows(src, r0, r1), kk,
+                                 stride, self._rows(dst, r0, r1))
 
     def _fill_full(self):
         cfg = self.cfg
@@ -155,8 +179,10 @@ class Workload:
             kmax = max(drop_lens)
             self.kept = torch.empty((B, L, Hkv, kmax + self.spare_tokens), dtype=torch.int32, device=self.dev)
             sel_lens = [n if k else 0 for n, k in zip(self.lens, drop_lens)]
-            vc.select_kept(self.shape, sel_lens, [r.recent for r in reqs], [r.top for r in reqs],
-                           scores, nmax, self.kept, self.kept.shape[-1])
+            for r0, r1 in self._chunks(B):
+                vc.select_kept(self.shape, sel_lens[r0:r1], [r.recent for r in reqs[r0:r1]],
+                               [r.top for r in reqs[r0:r1]], scores[r0:r1], nmax, self.kept[r0:r1],
+                               self.kept.shape[-1])
             if keep_scores:
                 self.scores = scores
             else:
@@ -164,7 +190,7 @@ class Workload:
         bf16_drop = [k if reqs[i].comp == C.COMP_DROP else 0 for i, k in enumerate(drop_lens)]
         if any(bf16_drop):
             self.drop_pool = self._bf16_pool(bf16_drop, salt=1, name="drop")
-            vc.compress(self.shape, bf16_drop, self.full, self.kept, self.kept.shape[-1], self.drop_pool)
+            self._compress(bf16_drop, self.full, self.kept, self.drop_pool)
         if any(kivi_lens):
             bits = {C.COMP_KIVI2: 2, C.COMP_DROP_KIVI4: 4}
             kinds = {reqs[i].comp for i, k in enumerate(kivi_lens) if k}
@@ -174,9 +200,9 @@ class Workload:
             with_kept = [k if reqs[i].comp == C.COMP_DROP_KIVI4 else 0 for i, k in enumerate(kivi_lens)]
             plain = [k if reqs[i].comp == C.COMP_KIVI2 else 0 for i, k in enumerate(kivi_lens)]
             if any(with_kept):
-                vc.compress(self.shape, with_kept, self.full, self.kept, self.kept.shape[-1], self.kivi_pool)
+                self._compress(with_kept, self.full, self.kept, self.kivi_pool)
             if any(plain):
-                vc.compress(self.shape, plain, self.full, None, 0, self.kivi_pool)
+                self._compress(plain, self.full, None, self.kivi_pool)
 
     def draft_pool_of(self, r: int) -> vc.PagedPool:
         comp = self.cfg.reqs[r].comp
@@ -295,10 +321,12 @@ class Workload:
         dropped = lambda r: self.drafts(r) and cfg.reqs[r].comp in (C.COMP_DROP, C.COMP_DROP_KIVI4)
         with_kept = [c for c in commits if dropped(c[0])]
         without = [c for c in commits if not dropped(c[0])]
-        if with_kept:   # token drop: the committed positions also join the kept lists
-            vc.commit_rows(self.shape, with_kept, self.blk_k, self.blk_v, self.full, kept, kept.shape[-1])
-        if without:
-            vc.commit_rows(self.shape, without, self.blk_k, self.blk_v, self.full)
+        step = vc.MAX_BATCH
+        for i in range(0, len(with_kept), step):   # token drop: committed positions join the kept lists
+            vc.commit_rows(self.shape, with_kept[i:i + step], self.blk_k, self.blk_v, self.full, kept,
+                           kept.shape[-1])
+        for i in range(0, len(without), step):
+            vc.commit_rows(self.shape, without[i:i + step], self.blk_k, self.blk_v, self.full)
         for name, pool, comps in (("drop", self.drop_pool, (C.COMP_DROP,)),
                                   ("kivi", self.kivi_pool, (C.COMP_KIVI2, C.COMP_DROP_KIVI4))):
             if pool is None:
@@ -313,8 +341,7 @@ class Workload:
                     frm.append(self.comp_lens[r] if uses else 0)
                     to.append(self.comp_lens[r] + c if uses else 0)
                 if any(t > f for f, t in zip(frm, to)):
-                    vc.compress_tail(self.shape, frm, to, self.full, kept if with_kept else None,
-                                     kept.shape[-1] if (with_kept and kept is not None) else 0, pool)
+                    self._compress(to, self.full, kept if with_kept else None, pool, from_lens=frm)
         for r, n, c, _, k in commits:
             self.lens[r] = n + c
             if self.drafts(r):
@@ -368,6 +395,35 @@ class Workload:
             self.run_draft(i)
         self.run_verify()
         self.logits_and_accept()
+
+    # ---------------------------------------------------------------- staging the full cache
+    def full_to_host(self):
+        """Copy the full pool's K and V into exact-size pinned host buffers (the host tier the full
+        cache is reloaded from).  Returns the two buffers; keep them alive while staging."""
+        from .pinned import PinnedBuffer
+        bufs = []
+        for t in (self.full.k, self.full.v):
+            b = PinnedBuffer(t.numel() * t.element_size())
+            b.tensor(t.dtype, t.shape).copy_(t)
+            bufs.append(b)
+        torch.cuda.synchronize(self.dev)
+        return bufs
+
+    def stage_full(self, bufs, side_stream, event, layers: Optional[int] = None):
+        """Enqueue the reload of the full pool from `bufs` (full_to_host) on `side_stream` with
+        vc_stage_kv, one copy per layer slice of K and of V, and record `event` after the last one.
+        layers: reload only layer slices [0, layers).  Returns the bytes enqueued."""
+        L = self.cfg.L if layers is None else layers
+        if event is not None:
+            event.record(side_stream)   # torch creates the HIP event on its first record
+        total = 0
+        for t, b in zip((self.full.k, self.full.v), bufs):
+            per = t[0].numel() * t.element_size()
+            host = b.tensor(t.dtype, t.shape)
+            for l in range(L):
+                vc.stage_kv(t[l], host[l], per, side_stream, event)
+                total += per
+        return total
 
     # ---------------------------------------------------------------- algorithmic bytes
     def verify_bytes(self) -> int:

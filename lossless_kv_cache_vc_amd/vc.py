@@ -15,10 +15,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIBVC_PATH = os.path.join(PKG, "libvc.so")
 
 VC_OK, VC_EINVAL, VC_ENOSPACE, VC_EHIP, VC_EUNSUPPORTED, VC_ENOMEM, VC_EAGAIN = 0, -1, -2, -3, -4, -5, -6
+VC_EDEVICE = -7
 PAGE_RESIDENT, PAGE_TRANSIENT = 0, 1
 VC_VERIFY, VC_DRAFT = 0, 1
 BLOCK = 16
-MAX_REQS = 64
+MAX_REQS = 1024      # requests per attention launch
+MAX_BATCH = 128      # requests per cache-building or commit call
 MAX_ROWS = 64
 
 # every symbol include/vc.h declares
@@ -30,7 +32,7 @@ EXPORTS = (
     "vc_alloc_release", "vc_alloc_free_count", "vc_page_row_extend", "vc_page_row_truncate",
     "vc_sched_create", "vc_sched_destroy", "vc_sched_admit", "vc_sched_advance", "vc_sched_now",
     "vc_sched_ring", "vc_sched_due",
-    "vc_last_error", "vc_version",
+    "vc_check_device", "vc_last_error", "vc_version",
 )
 
 
@@ -99,6 +101,7 @@ def lib():
         L.vc_select_kept.argtypes = [P(Shape), i32, vp, vp, vp, vp, i64, vp, i64, vp]
         L.vc_compress.argtypes = [P(Shape), i32, vp, P(Pool), vp, i64, P(Pool), vp]
         L.vc_stage_kv.argtypes = [vp, vp, sz, vp, vp]
+        L.vc_check_device.argtypes = [vp]
         L.vc_commit_rows.argtypes = [P(Shape), i32, P(Commit), vp, vp, P(Pool), vp, i64, vp]
         L.vc_compress_tail.argtypes = [P(Shape), i32, vp, vp, P(Pool), vp, i64, P(Pool), vp]
         L.vc_alloc_create.argtypes = [ctypes.c_int32, ctypes.c_int32, P(vp)]
@@ -253,8 +256,18 @@ def compress(shp, comp_lens, src: PagedPool, kept, kept_stride, dst: PagedPool, 
 
 
 def stage_kv(dst, src_pinned, nbytes, side_stream, event=None):
+    """event: a torch.cuda.Event that has been recorded once (torch creates the HIP event on its
+    first record; before that it has no handle to pass)."""
     ev = None if event is None else event.cuda_event
+    if event is not None and not ev:
+        raise ValueError("stage_kv: the event has no HIP handle yet; record it once first")
     _check(lib().vc_stage_kv(_ptr(dst), _ptr(src_pinned), nbytes, _stream(side_stream), ev))
+
+
+def check_device(stream=None):
+    """Synchronise `stream` and raise VCError(VC_EDEVICE) if a kernel met a corrupt page-table
+    entry since the last check (the device error word is then cleared)."""
+    _check(lib().vc_check_device(_stream(stream)))
 
 
 def version() -> str:

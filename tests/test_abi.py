@@ -136,3 +136,52 @@ def test_stream_probe_library_loads_and_rejects_bad_arguments():
     assert L.vcprobe_read(0x1000, 24, 1, 0x3000, None) == -1                     # not 16-byte pieces
     assert L.vcprobe_read(0x1000, 16, 0, 0x3000, None) == -1                     # no groups
     assert L.vcprobe_read(0x1000, 16, 1, None, None) == -1
+
+
+def test_status_codes_and_limits_agree_with_the_header():
+    src = open(os.path.join(ROOT, "include", "vc.h")).read()
+    codes = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"\b(VC_E[A-Z]+|VC_OK)\s*=\s*(-?\d+)", src))
+    for name, val in codes.items():
+        assert getattr(vc, name) == val, name
+    assert codes["VC_EDEVICE"] == -7
+    limits = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"#define (VC_MAX_[A-Z]+) (\d+)", src))
+    assert limits == {"VC_MAX_REQS": vc.MAX_REQS, "VC_MAX_BATCH": vc.MAX_BATCH, "VC_MAX_ROWS": vc.MAX_ROWS}
+
+
+def test_workspace_holds_the_request_table_of_large_launches():
+    """More than 64 requests: the launch's request table (56 bytes per request, rounded up to
+    256) heads the workspace, before any split partials; 64 or fewer ride in the kernel
+    arguments."""
+    shp = _shape()
+    r = vc.Req(0, 0, 16 * 10, 0, 0, 8, vc.VC_VERIFY)
+    assert vc.attn_workspace_size(shp, [r] * 64, 400) == 0
+    assert vc.attn_workspace_size(shp, [r] * 65, 400) == (65 * 56 + 255) // 256 * 256
+    assert vc.attn_workspace_size(shp, [r] * 1024, 400) == 1024 * 56
+    assert vc.attn_workspace_size(shp, [r] * 1025, 400) == 0          # rejected
+    split = vc.attn_workspace_size(shp, [r], 4)                         # 3 splits of one request
+    assert vc.attn_workspace_size(shp, [r] * 100, 4) == (100 * 56 + 255) // 256 * 256 + 100 * split
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device pointers; host-only check")
+def test_large_launches_validate_on_host():
+    t = _FakeTensor(0x1000)
+    r = vc.Req(0, 0, 100, 0, 0, 8, vc.VC_VERIFY)
+    _expect(vc.VC_EINVAL, lambda: vc.verify_attn(_shape(), [r] * 1025, t, t, t, _pool(), t, None, 0, 0))
+    # 65 requests need the workspace for their table
+    _expect(vc.VC_ENOSPACE, lambda: vc.verify_attn(_shape(), [r] * 65, t, t, t, _pool(), t, None, 0, 0))
+    ws = _FakeTensor(0x2000, (16,))
+    ws.numel, ws.element_size = (lambda: 16), (lambda: 4)   # 64 bytes: too small
+    _expect(vc.VC_ENOSPACE, lambda: vc.verify_attn(_shape(), [r] * 65, t, t, t, _pool(), t, ws, 0, 0))
+    # build and commit calls take at most 128 requests
+    _expect(vc.VC_EINVAL, lambda: vc.compress(_shape(), [16] * 129, _pool(), None, 0, _pool(), 0))
+    _expect(vc.VC_EINVAL, lambda: vc.select_kept(_shape(), [16] * 129, [0] * 129, [4] * 129, t, 16, t, 16, 0))
+    _expect(vc.VC_EINVAL, lambda: vc.commit_rows(_shape(), [(0, 0, 1, 0, 0)] * 129, t, t, _pool(), None, 0, 0))
+
+
+def test_stage_kv_checks_its_arguments_on_the_host():
+    """bytes == 0 enqueues no copy (and, without an event, touches no device); NULL pointers with
+    bytes > 0 are rejected before any HIP call."""
+    lib = vc.lib()
+    assert lib.vc_stage_kv(None, None, 0, None, None) == vc.VC_OK
+    assert lib.vc_stage_kv(None, 0x1000, 64, None, None) == vc.VC_EINVAL
+    assert lib.vc_stage_kv(0x1000, None, 64, None, None) == vc.VC_EINVAL
