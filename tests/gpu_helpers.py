@@ -11,15 +11,30 @@ from vcsynth import configs as C
 TOL_CONTRACT = 5e-3   # max-abs bound on attention outputs (the contract)
 
 
+# Relative error scale of one softmax weight as it enters the value product, per path.
+#  * bf16 caches: the weight is rounded to bf16 (unit roundoff 2^-9).
+#  * KIVI caches: three fp16 roundings (unit roundoff 2^-11), added in quadrature:
+#      - the weight itself (fp16 operand of the value product);
+#      - the weight times the token's value scale (the folded scale, one more rounding);
+#      - the score: each channel's term code_c * fp16(q_c * s_c) carries a rounding of at most
+#        2^-11 of itself; with N(0,1) data the terms code_c * s_c = k_c - min(group) have
+#        E[(k - min)^2] ~ 5 over groups of 32 (min ~ -2, variance 1), so over d channels the
+#        score error (in units of the softmax exponent, after the 1/sqrt(d) scale) has scale
+#        2^-11 * sqrt(5 d) / sqrt(d) = 2^-11 * sqrt(5), a relative error of the weight.
+#    sqrt(1 + 1 + 5) * 2^-11 ~ 1.3e-3, below the bf16 path's 2^-9 ~ 1.95e-3.
+WEIGHT_REL_BF16 = 2.0 ** -9
+WEIGHT_REL_KIVI = 2.0 ** -11 * np.sqrt(1.0 + 1.0 + 5.0)
+
+
 def tight_tol(n_keys: int, kivi: bool = False) -> float:
-    """Internal gate derived from the kernel's arithmetic.  The value product multiplies softmax
-    weights rounded to bf16 (relative error uniform within +-2^-8, standard deviation about
-    2^-9), so with N(0,1) values an output element carries an error of about
-    2^-9 * sqrt(e / n_keys) (softmax over N(0,1) scores has about n_keys / e effective keys).
-    The gate allows 12 of those plus 1e-4: ~3e-4 at 32K keys, ~4e-3 at 100 keys, never above
-    the contract.  The KIVI path rounds its dequantised keys, values and weights to fp16
-    (2^-11) instead, which keeps it inside the same gate."""
-    base = 2.0 ** -9 * np.sqrt(np.e / max(1, n_keys))
+    """Internal gate derived from the kernel's arithmetic.  Softmax weights enter the value
+    product with a relative error of scale eps (WEIGHT_REL_BF16 or WEIGHT_REL_KIVI), so with
+    N(0,1) values an output element carries an error of about eps * sqrt(e / n_keys) (softmax
+    over N(0,1) scores has about n_keys / e effective keys).  The gate allows 12 of those plus
+    1e-4 (fp32 accumulation over the keys): ~3e-4 at 32K keys on the bf16 path, ~4e-3 at 100
+    keys, never above the contract."""
+    eps = WEIGHT_REL_KIVI if kivi else WEIGHT_REL_BF16
+    base = eps * np.sqrt(np.e / max(1, n_keys))
     return float(min(TOL_CONTRACT, 12 * base + 1e-4))
 
 

@@ -187,7 +187,7 @@ def test_mixed_ragged_parity():
                          f"C5 draft r={r} ({req.comp}, step {req.step})")
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C4"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4"])
 def test_tokens_and_accept(name):
     cfg, wl = built(name)
     tok_d = wl.tok_d.cpu().numpy()
@@ -214,3 +214,25 @@ def test_tokens_and_accept(name):
             assert np.array_equal(tok_d[inst, :x], td) and np.array_equal(tok_v[inst, :x], tv)
             assert (alen[inst], nxt[inst]) == oacc.accept(td, tv)
     print(f"{name}: {flagged} flagged accept lengths of {cfg.B * cfg.L}")
+
+
+def test_mixed_ragged_tokens():
+    """Tokens of the ragged mixed launch: the LM-head stand-in and the accept kernel's argmax over
+    every verify row of the verifying requests and the draft-step row of the drafting ones,
+    against the oracle's tokens (flagged near-ties excepted)."""
+    cfg, wl = built("C5")
+    wl.logits_and_accept()
+    torch.cuda.synchronize()
+    tok = wl.tok_v.cpu().numpy().reshape(cfg.B, wl.xmax)
+    wu = bf16_to_f64(T.wu_bits(cfg))
+    checked = 0
+    for r, req in enumerate(cfg.reqs):
+        if req.kind == C.KIND_VERIFY:
+            rows, o = list(range(req.x)), ow.verify_out(cfg, r, 0)
+        else:
+            rows, o = [req.step], ow.draft_out(cfg, r, 0, [req.step])
+        z = oacc.logits(o.reshape(len(rows), -1), wu)
+        t, gap = oacc.argmax_gap(z)
+        assert not tokens_match(tok[r, rows], t, gap, z), f"C5 tokens r={r}"
+        checked += len(rows)
+    print(f"C5: {checked} token rows checked")
