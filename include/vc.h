@@ -165,6 +165,24 @@ int vc_attn_mixed(const vc_shape* shape, int num_reqs, const vc_req* reqs /* hos
                   float* out, void* workspace, size_t workspace_bytes, int split_pages, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): vc_attn_mixed without a workspace argument.  The
+ * workspace comes from a device array the library holds, VC_SCRATCH_BYTES on each device it runs
+ * on, from the first call on that device until the process ends; the call allocates nothing.
+ * Every output is what vc_attn_mixed writes for the same arguments.
+ * Errors: as vc_attn_mixed; VC_ENOSPACE (nothing enqueued) when the launch needs more workspace
+ * than VC_SCRATCH_BYTES (vc_attn_workspace_size tells; long contexts split many ways need more).
+ * The array is shared by every call on a device and keeps the last call's contents (every call
+ * writes what it reads, so nothing needs clearing): calls that overlap on one device (other
+ * streams, other threads) race and must be ordered by the caller.
+ */
+#define VC_SCRATCH_BYTES (64u << 20)
+int vc_attn_mixed_noalloc(const vc_shape* shape, int num_reqs, const vc_req* reqs /* host */,
+                          const void* q, const void* blk_k, const void* blk_v,
+                          int num_pools, const vc_pool* pools /* host array */,
+                          float* out, int split_pages, void* stream);
+
+/*
  * Greedy accept (VeriCache review, §Draft–Verify Pipeline steps 5–6) for n_inst independent
  * drafted blocks.  For instance i: x[i] drafted rows (1..max_x), xv[i] verifier rows (x[i], or
  * x[i]+1 where the extra row gives the bonus token; at most max_xv).  Logits rows are contiguous

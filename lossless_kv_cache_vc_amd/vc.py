@@ -25,7 +25,8 @@ MAX_ROWS = 64
 
 # every symbol include/vc.h declares
 EXPORTS = (
-    "vc_attn_workspace_size", "vc_verify_attn", "vc_draft_attn", "vc_attn_mixed", "vc_accept",
+    "vc_attn_workspace_size", "vc_verify_attn", "vc_draft_attn", "vc_attn_mixed", "vc_attn_mixed_noalloc",
+    "vc_accept",
     "vc_sample_tokens", "vc_accept_sampled",
     "vc_logits", "vc_pack_bf16", "vc_select_kept", "vc_compress", "vc_stage_kv",
     "vc_commit_rows", "vc_compress_tail", "vc_alloc_create", "vc_alloc_destroy", "vc_alloc_pages",
@@ -92,6 +93,7 @@ def lib():
         L.vc_verify_attn.argtypes = attn
         L.vc_draft_attn.argtypes = attn
         L.vc_attn_mixed.argtypes = [P(Shape), i32, P(Req), vp, vp, vp, i32, P(Pool), vp, vp, sz, i32, vp]
+        L.vc_attn_mixed_noalloc.argtypes = [P(Shape), i32, P(Req), vp, vp, vp, i32, P(Pool), vp, i32, vp]
         L.vc_accept.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.vc_logits.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp]
         L.vc_sample_tokens.argtypes = [i32, i32, ctypes.c_float, vp, vp, vp, vp]
@@ -211,6 +213,18 @@ def attn_mixed(shp, reqs, q, blk_k, blk_v, pools: Sequence[PagedPool], out, work
     _check(lib().vc_attn_mixed(ctypes.byref(shp), len(reqs), arr, _ptr(q), _ptr(blk_k), _ptr(blk_v),
                                len(pools), parr, _ptr(out), _ptr(workspace), ws, split_pages,
                                _stream(stream)))
+
+
+SCRATCH_BYTES = 64 << 20   # the library-held workspace of attn_mixed_noalloc, per device
+
+
+def attn_mixed_noalloc(shp, reqs, q, blk_k, blk_v, pools: Sequence[PagedPool], out, split_pages=0,
+                       stream=None):
+    arr = reqs_array(reqs)
+    parr = (Pool * len(pools))(*[p.desc() for p in pools])
+    _check(lib().vc_attn_mixed_noalloc(ctypes.byref(shp), len(reqs), arr, _ptr(q), _ptr(blk_k),
+                                       _ptr(blk_v), len(pools), parr, _ptr(out), split_pages,
+                                       _stream(stream)))
 
 
 def accept(n_inst, max_x, max_xv, vocab, x, xv, draft_logits, verify_logits, draft_tok, verify_tok,

@@ -185,3 +185,17 @@ def test_stage_kv_checks_its_arguments_on_the_host():
     assert lib.vc_stage_kv(None, None, 0, None, None) == vc.VC_OK
     assert lib.vc_stage_kv(None, 0x1000, 64, None, None) == vc.VC_EINVAL
     assert lib.vc_stage_kv(0x1000, None, 64, None, None) == vc.VC_EINVAL
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device pointers; host-only check")
+def test_noalloc_launch_refuses_on_the_host():
+    """vc_attn_mixed_noalloc sizes its launch before touching a device: beyond the library's
+    scratch array (VC_SCRATCH_BYTES) it returns VC_ENOSPACE; with nothing to do it returns OK."""
+    t = _FakeTensor(0x1000)
+    shp = _shape(max_rows=16)
+    r = vc.Req(0, 0, 16 * 8, 0, 0, 8, vc.VC_VERIFY)
+    many = [r] * 1024                      # 2 splits x 2 kv heads x 32 rows x 132 floats each
+    assert vc.attn_workspace_size(shp, many, 4) > vc.SCRATCH_BYTES
+    _expect(vc.VC_ENOSPACE, lambda: vc.attn_mixed_noalloc(shp, many, t, t, t, [_pool()], t, 4, 0))
+    vc.attn_mixed_noalloc(shp, [], t, t, t, [_pool()], t, 0, 0)
+    _expect(vc.VC_EINVAL, lambda: vc.attn_mixed_noalloc(shp, [r] * 1025, t, t, t, [_pool()], t, 0, 0))
