@@ -1813,8 +1813,26 @@ __device__ __forceinline__ bool decode_item(const AttnArgs& a, ItemCtx* it, int*
     rq = a.reqs[r];
   }
   int local = item - rq.item_base;
-  *rg = local % rq.nrg;
-  local /= rq.nrg;
+  if (a.xcd_ranges || rq.nrg == 1) {
+    *rg = local % rq.nrg;
+    local /= rq.nrg;
+  } else {
+    // work-group b takes item b (ragged batches): the row groups of one unit are placed 8 items
+    // apart, so they run on one XCD at about the same time and share its L2; consecutive units
+    // still go to different XCDs
+    const int R = rq.nrg;
+    const int U = a.L * a.Hkv * rq.nsplit;  // units of this request
+    const int full = U & ~7;
+    if (local < full * R) {
+      const int rem = local % (8 * R);
+      *rg = rem >> 3;
+      local = (local / (8 * R)) * 8 + (rem & 7);
+    } else {
+      const int t = U - full, j = local - full * R;
+      *rg = j / t;
+      local = full + j % t;
+    }
+  }
   const int split = local % rq.nsplit;
   local /= rq.nsplit;
   it->rq = rq;
