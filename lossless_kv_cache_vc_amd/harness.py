@@ -8,6 +8,7 @@ stand-in and the greedy accept — the per-request cycle of the VeriCache review
 """
 from __future__ import annotations
 
+import weakref
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
@@ -22,6 +23,19 @@ from vcsynth.configs import NPOS, XMAX
 from . import vc
 
 BF16 = torch.bfloat16
+
+# Guard regions around the tensors the kernels write (pools, outputs, workspaces, kept lists,
+# logits, tokens) when VC_CANARY=1: each such tensor is a view into a larger buffer whose first and
+# last CANARY_BYTES hold CANARY_BYTE, and check_canaries() reports any guard byte that changed (a
+# write past either end).  Off by default; the tests turn it on.
+CANARY_BYTES = 64 * 1024
+CANARY_BYTE = 0xA5
+_GUARDED: "weakref.WeakSet" = None
+
+
+def _canary_on() -> bool:
+    import os
+    return os.environ.get("VC_CANARY") == "1"
 
 
 def round16(x: int) -> int:
@@ -45,6 +59,13 @@ class Workload:
         """spare_tokens: growth room per request in every pool (page-table width, blocks handed
         out by the library's page allocator, kept-list width) for committing accepted rows."""
         self.cfg = cfg
+        self._canary = _canary_on()
+        self._guards = []
+        if self._canary:
+            global _GUARDED
+            if _GUARDED is None:
+                _GUARDED = weakref.WeakSet()
+            _GUARDED.add(self)
         self.spare_pages = (spare_tokens + 15) // 16 + (1 if spare_tokens else 0)
         self.spare_tokens = spare_tokens
         self._grow = {}
@@ -73,14 +94,41 @@ class Workload:
             self.full = self._bf16_pool(self.lens, salt=0, name="full")
             self._fill_full()
 
-            self.out_v = torch.zeros((B, L, xm, Hq, d), dtype=torch.float32, device=dev)
-            self.out_d = torch.zeros((B, L, xm, Hq, d), dtype=torch.float32, device=dev)
+            self.out_v = self._out((B, L, xm, Hq, d), torch.float32, zero=True)
+            self.out_d = self._out((B, L, xm, Hq, d), torch.float32, zero=True)
             self.drop_pool: Optional[vc.PagedPool] = None
             self.kivi_pool: Optional[vc.PagedPool] = None
             self.kept: Optional[torch.Tensor] = None
             if build_compressed:
                 self._build_compressed(keep_dense_scores)
             self.workspace = self._workspace()
+
+    # ---------------------------------------------------------------- guarded allocations
+    def _out(self, shape, dtype, zero: bool = False) -> torch.Tensor:
+        """A tensor the kernels write: inside guard regions when canaries are on."""
+        if not self._canary:
+            return (torch.zeros if zero else torch.empty)(shape, dtype=dtype, device=self.dev)
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        G = CANARY_BYTES
+        buf = torch.empty(n + 2 * G, dtype=torch.uint8, device=self.dev)
+        buf[:G].fill_(CANARY_BYTE)
+        buf[G + n:].fill_(CANARY_BYTE)
+        t = buf[G:G + n].view(dtype).view(shape)
+        if zero:
+            t.zero_()
+        self._guards.append((buf, n))
+        return t
+
+    def check_canaries(self):
+        """Raise AssertionError if a guard byte around a written tensor changed."""
+        G = CANARY_BYTES
+        for i, (buf, n) in enumerate(self._guards):
+            lo, hi = buf[:G], buf[G + n:]
+            if not (bool((lo == CANARY_BYTE).all()) and bool((hi == CANARY_BYTE).all())):
+                bad_lo = int((lo != CANARY_BYTE).sum())
+                bad_hi = int((hi != CANARY_BYTE).sum())
+                raise AssertionError(f"guard bytes changed around written tensor {i} ({n} bytes): "
+                                     f"{bad_lo} before it, {bad_hi} after it")
 
     # ---------------------------------------------------------------- pools
     def _tables(self, lens: List[int], salt: int, name: str):
@@ -99,18 +147,18 @@ class Workload:
         cfg = self.cfg
         pt, nblk = self._tables(lens, salt, name)
         shape = (cfg.L, nblk, cfg.Hkv, 16, cfg.d)
-        k = torch.empty(shape, dtype=BF16, device=self.dev)
-        v = torch.empty(shape, dtype=BF16, device=self.dev)
+        k = self._out(shape, BF16)
+        v = self._out(shape, BF16)
         return vc.PagedPool(16, torch.from_numpy(pt).to(self.dev), k, v, nblk)
 
     def _kivi_pool(self, lens: List[int], bits: int, salt: int, name: str = "") -> vc.PagedPool:
         cfg = self.cfg
         pt, nblk = self._tables(lens, salt, name)
         d, L, Hkv = cfg.d, cfg.L, cfg.Hkv
-        k = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
-        v = torch.empty((L, nblk, Hkv, 16 * d * bits // 8), dtype=torch.uint8, device=self.dev)
-        ksz = torch.empty((L, nblk, Hkv, 2, d), dtype=torch.int16, device=self.dev)
-        vsz = torch.empty((L, nblk, Hkv, d // 32, 2, 16), dtype=torch.int16, device=self.dev)
+        k = self._out((L, nblk, Hkv, 16 * d * bits // 8), torch.uint8)
+        v = self._out((L, nblk, Hkv, 16 * d * bits // 8), torch.uint8)
+        ksz = self._out((L, nblk, Hkv, 2, d), torch.int16)
+        vsz = self._out((L, nblk, Hkv, d // 32, 2, 16), torch.int16)
         return vc.PagedPool(bits, torch.from_numpy(pt).to(self.dev), k, v, nblk, ksz, vsz)
 
     @staticmethod
@@ -177,7 +225,7 @@ class Workload:
             scores = torch.empty((B, L, Hkv, nmax), dtype=torch.int32, device=self.dev)
             sg.fill_u32(scores, [L * Hkv * NPOS, Hkv * NPOS, NPOS, 1], 0, cfg.seed, rng.STREAM_SCORE)
             kmax = max(drop_lens)
-            self.kept = torch.empty((B, L, Hkv, kmax + self.spare_tokens), dtype=torch.int32, device=self.dev)
+            self.kept = self._out((B, L, Hkv, kmax + self.spare_tokens), torch.int32)
             sel_lens = [n if k else 0 for n, k in zip(self.lens, drop_lens)]
             for r0, r1 in self._chunks(B):
                 vc.select_kept(self.shape, sel_lens[r0:r1], [r.recent for r in reqs[r0:r1]],
@@ -245,7 +293,7 @@ class Workload:
                         need = max(need, vc.attn_workspace_size(self.shape, rq))
         if need == 0:
             return None
-        return torch.empty(need // 4 + 1, dtype=torch.float32, device=self.dev)
+        return self._out((need // 4 + 1,), torch.float32)
 
     # ---------------------------------------------------------------- passes
     def run_verify(self, split_pages: int = 0, out: Optional[torch.Tensor] = None):
@@ -277,7 +325,7 @@ class Workload:
         cache = getattr(self, "_ws_cache", {})
         t = cache.get(key)
         if t is None or t.numel() * 4 < need:
-            t = torch.empty(need // 4 + 1, dtype=torch.float32, device=self.dev)
+            t = self._out((need // 4 + 1,), torch.float32)
             cache[key] = t
             self._ws_cache = cache
         return t
@@ -355,14 +403,14 @@ class Workload:
         width = cfg.Hq * cfg.d
         rows = B * L * xm
         if not hasattr(self, "z_v"):
-            self.z_v = torch.empty((rows, V), dtype=torch.float32, device=self.dev)
-            self.z_d = torch.empty((rows, V), dtype=torch.float32, device=self.dev)
+            self.z_v = self._out((rows, V), torch.float32)
+            self.z_d = self._out((rows, V), torch.float32)
             xs = torch.tensor([cfg.reqs[r].x for r in range(B) for _ in range(L)], dtype=torch.int32)
             self.x_dev = xs.to(self.dev)
-            self.tok_d = torch.empty((B * L, xm), dtype=torch.int32, device=self.dev)
-            self.tok_v = torch.empty((B * L, xm), dtype=torch.int32, device=self.dev)
-            self.acc_len = torch.empty(B * L, dtype=torch.int32, device=self.dev)
-            self.next_tok = torch.empty(B * L, dtype=torch.int32, device=self.dev)
+            self.tok_d = self._out((B * L, xm), torch.int32)
+            self.tok_v = self._out((B * L, xm), torch.int32)
+            self.acc_len = self._out((B * L,), torch.int32)
+            self.next_tok = self._out((B * L,), torch.int32)
         vc.logits(rows, width, V, self.out_v, width, self.w_u, self.z_v)
         vc.logits(rows, width, V, self.out_d, width, self.w_u, self.z_d)
 
@@ -471,3 +519,12 @@ class Workload:
                 tot += cfg.L * cfg.Hq * cfg.d * 6
             tot += _pages(r.ctx_len) * 4
         return tot
+
+
+def check_all_canaries():
+    """Check the guard regions of every live workload built with canaries (VC_CANARY=1)."""
+    if _GUARDED is None:
+        return
+    torch.cuda.synchronize()
+    for wl in list(_GUARDED):
+        wl.check_canaries()

@@ -128,3 +128,23 @@ def test_pack_never_writes_through_a_corrupt_entry():
             assert torch.equal(kk[0, b], ss[0, :, 16 * p:16 * p + 16]), p
     for b in (1, 2, 4, 5, 7):   # never named by a valid entry
         assert torch.all(kk[0, b] == 7.0), b
+
+
+def test_guard_regions_catch_a_write_past_a_tensor():
+    """The guard regions the harness puts around every written tensor (VC_CANARY=1 in the tests)
+    report a changed byte: one guard byte is overwritten from the host (a torch write into the
+    guard, no kernel involved), the check must fail, and pass again once it is restored."""
+    require_gpu()
+    from lossless_kv_cache_vc_amd import harness
+    from lossless_kv_cache_vc_amd.harness import Workload
+    assert harness._canary_on(), "the tests run with guard regions"
+    cfg = C.scaled(C.get("C2"), L=1, B=1, n=200, x=8)
+    wl = Workload(cfg, build_compressed=False)
+    wl.run_verify()
+    wl.check_canaries()
+    buf, n = wl._guards[-1]
+    buf[harness.CANARY_BYTES + n + 7] = 0          # just past the end of that tensor
+    with pytest.raises(AssertionError, match="1 after it"):
+        wl.check_canaries()
+    buf[harness.CANARY_BYTES + n + 7] = harness.CANARY_BYTE
+    wl.check_canaries()
