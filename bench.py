@@ -39,8 +39,8 @@ TIE_GAP = 1e-3  # a logits row whose top-2 gap is below this is a near-tie (flag
 
 def measured_traffic(config: str, kind: str):
     """HBM bytes per launch of one attention kernel of one workload from the committed rocprofv3
-    counter runs (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when
-    absent or taken on other kernel code."""
+    counter runs (L2-to-memory read and write requests counted by size, checked exactly on a
+    device copy of known size), or None when absent or taken on other kernel code."""
     from lossless_kv_cache_vc_amd.profiling import attn_source_hash
     try:
         rec = json.load(open(TRAFFIC_FILE))

@@ -128,6 +128,72 @@ def cmd_traffic(args):
     print("\n".join(lines))
 
 
+def _req_bytes(reads: Dict[str, List[float]], writes: Dict[str, List[float]]):
+    """Read and write bytes per dispatch from the request-size counters: each read request is 32,
+    64 or 128 bytes (TCC_EA0_RDREQ_32B/_64B/_128B), each write 32 or 64 bytes (TCC_EA0_WRREQ minus
+    TCC_EA0_WRREQ_64B, and TCC_EA0_WRREQ_64B); lists are per dispatch."""
+    n32, n64, n128 = (reads.get(f"TCC_EA0_RDREQ_{k}_sum", []) for k in ("32B", "64B", "128B"))
+    tot = reads.get("TCC_EA0_RDREQ_sum", [])
+    wr, w64 = writes.get("TCC_EA0_WRREQ_sum", []), writes.get("TCC_EA0_WRREQ_64B_sum", [])
+    rd_b = [32 * a + 64 * b + 128 * c for a, b, c in zip(n32, n64, n128)]
+    wr_b = [32 * (a - b) + 64 * b for a, b in zip(wr, w64)]
+    unsized = [t - (a + b + c) for t, a, b, c in zip(tot, n32, n64, n128)]
+    return rd_b, wr_b, unsized
+
+
+def cmd_traffic_req(args):
+    """HBM bytes per launch from request-size counters (no fitted scale): the copy probe's counted
+    bytes are compared with its true bytes as a check of the counters, not used as a factor."""
+    reads = _counters(os.path.join(args.reads, "*counter_collection.csv"))
+    writes = _counters(os.path.join(args.writes, "*counter_collection.csv"))
+    creads = _counters(os.path.join(args.copy_reads, "*counter_collection.csv"))
+    cwrites = _counters(os.path.join(args.copy_writes, "*counter_collection.csv"))
+    # the copy is the dispatch that reads the most (the probe also runs a fill first)
+    copy_name = max(creads, key=lambda n: max(creads[n].get("TCC_EA0_RDREQ_sum", [0.0])), default=None)
+    cr, cw, cu = _req_bytes(creads.get(copy_name, {}), cwrites.get(copy_name, {}))
+    copy_read = max(cr) if cr else 0.0
+    copy_write = max(cw) if cw else 0.0
+    check_r = copy_read / args.copy_bytes if args.copy_bytes else None
+    check_w = copy_write / args.copy_bytes if args.copy_bytes else None
+    try:
+        rec = json.load(open(args.json))
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_hash") != attn_source_hash():
+        rec = {}
+    rec.update({"source_hash": attn_source_hash(), "method": "request-size counters (32/64/128-byte reads, "
+                "32/64-byte writes)", "copy_bytes": args.copy_bytes,
+                "copy_check": {"read_ratio": None if check_r is None else round(check_r, 4),
+                               "write_ratio": None if check_w is None else round(check_w, 4)}})
+    rec.setdefault("configs", {})
+    entry = {"command": args.cmd, "kernels": {}}
+    rec["configs"][args.config] = entry
+    lines = [f"# {args.title}", "", "Commands (request-size counters; reads and writes in separate runs, then the "
+             "same for the copy probe):", "", "```", args.cmd, "```", "",
+             f"Bytes = 32 x TCC_EA0_RDREQ_32B + 64 x TCC_EA0_RDREQ_64B + 128 x TCC_EA0_RDREQ_128B (reads) and "
+             f"32 x (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) + 64 x TCC_EA0_WRREQ_64B (writes), summed over the L2 "
+             f"channels, per dispatch.  Check on a {args.copy_bytes / 2**30:.0f} GiB device copy: "
+             f"{copy_read / 2**30:.4f} GiB read and {copy_write / 2**30:.4f} GiB written by these counters "
+             f"(ratios {check_r:.4f} and {check_w:.4f}); requests the size counters do not classify: "
+             f"{int(max(cu) if cu else 0)}.", "",
+             "| kernel | launches | read bytes/launch | write bytes/launch | HBM bytes/launch | unsized read requests |",
+             "|---|---|---|---|---|---|"]
+    for name in sorted(set(reads) | set(writes)):
+        role = _role(name)
+        if role is None:
+            continue
+        rb, wb, un = _req_bytes(reads[name], writes.get(name, {}))
+        r, w = _avg(rb), _avg(wb)
+        entry["kernels"][role] = {"bytes_per_launch": int(r + w), "read_bytes": int(r), "write_bytes": int(w),
+                                  "launches": len(rb), "unsized_read_requests": _avg(un)}
+        lines.append(f"| {role} | {len(rb)} | {r:.4g} | {w:.4g} | {r + w:.4g} | {_avg(un):.0f} |")
+    if args.note:
+        lines += ["", args.note]
+    json.dump(rec, open(args.json, "w"), indent=1)
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cmd_sq(args):
     c = _counters(os.path.join(args.dir, "*", "*counter_collection.csv"))
     lines = [f"# {args.title}", "", "Commands:", "", "```", args.cmd, "```", "",
@@ -165,6 +231,17 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--note", default="")
     t.set_defaults(fn=cmd_traffic)
+    r = sub.add_parser("traffic-req")
+    for k in ("reads", "writes", "copy_reads", "copy_writes"):
+        r.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    r.add_argument("--copy-bytes", type=int, required=True)
+    r.add_argument("--config", required=True, help="workload id the counters were taken on (e.g. C2)")
+    r.add_argument("--json", required=True)
+    r.add_argument("--out", required=True)
+    r.add_argument("--title", default="HBM traffic per launch")
+    r.add_argument("--cmd", required=True)
+    r.add_argument("--note", default="")
+    r.set_defaults(fn=cmd_traffic_req)
     q = sub.add_parser("sq")
     q.add_argument("--dir", required=True)
     q.add_argument("--out", required=True)
