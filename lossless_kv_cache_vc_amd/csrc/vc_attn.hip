@@ -1418,6 +1418,45 @@ struct KRing {
   static constexpr int kStg = kStg0 > 8 ? 8 : kStg0;        // slots per wave
   static constexpr int kBytes = kIds + kMaxChunkPages * 4 + 16;  // ids, then the first missing page
   static_assert(kParams % 16 == 0 && kParams <= 1024, "the parameters of a pair are one load");
+  // LDS layout of a slot's codes (64 banks of 4 bytes).  The ring is written lane-linearly, 16
+  // bytes per lane, so a layout is a permutation of 16-byte chunks chosen by which global chunk a
+  // lane fetches.  One read takes rows of both pages at once (key rows 4 b + i and 8 + 4 b + i,
+  // value channels 16 db + n), and the two pages of a pair would sit a multiple of the bank span
+  // apart.  So the pages' codes are interleaved in 128-byte blocks (block q of the even page, then
+  // block q of the odd page): a row of the odd page is always 128 bytes after the same row of the
+  // even page, on the other half of the banks, and every read is a per-lane base plus a constant.
+  // Key rows t and t + 8, which land on the same banks, also have their chunks permuted
+  // (krow_xor).  The scale and zero planes are read one address per 16 lanes (broadcast).
+  static constexpr int kCPR = D * BITS / 8 / 16;  // 16-byte chunks of a key row
+  static constexpr int kRowB = 16 * kCPR;         // bytes of a key row
+  static constexpr int kRPB = kRowB >= 128 ? 1 : 128 / kRowB;  // key rows per 128-byte block
+  static_assert(kRowB <= 128 && kCodes % 128 == 0, "pages interleave in 128-byte blocks");
+  static __device__ __forceinline__ int krow_xor(int t) {
+    if constexpr (kCPR >= 4) return ((t >> 1) & 1) | (((t >> 3) & 1) << 1);
+    else if constexpr (kCPR == 2) return (t >> 3) & 1;
+    else return 0;
+  }
+  // LDS byte offset (inside the slot's key codes) of chunk j of token row t of page `page`
+  static __device__ __forceinline__ int kcode_pos(int page, int t, int j) {
+    return 256 * (t / kRPB) + 128 * page + kRowB * (t % kRPB) + 16 * (j ^ krow_xor(t));
+  }
+  // key rows 4 b on: kcode_pos(p, t + 4 b, j) = kcode_pos(p, t, j) + b * kKeyStepB when bit 2 of t is clear
+  static constexpr int kKeyStepB = kRPB >= 8 ? 4 * kRowB : 256 * (4 / kRPB);
+  // the global byte offset (page, offset inside the page) of the chunk at LDS byte B of the key codes
+  static __device__ __forceinline__ int kcode_src(int B, int* page) {
+    const int q = B >> 8, r = B & 255;
+    *page = r >> 7;
+    const int tt = q * kRPB + (r & 127) / kRowB;
+    const int jj = ((r & 127) % kRowB) >> 4;
+    return tt * kRowB + 16 * (jj ^ krow_xor(tt));
+  }
+  // value codes: byte o of page `page` sits at LDS byte vcode_pos(page, o)
+  static constexpr int kVRow = kBlock * BITS / 8;  // bytes of a value channel row
+  static __device__ __forceinline__ int vcode_pos(int page, int o) { return 256 * (o >> 7) + 128 * page + (o & 127); }
+  static __device__ __forceinline__ int vcode_src(int B, int* page) {
+    *page = (B >> 7) & 1;
+    return 128 * (B >> 8) + (B & 127);
+  }
 };
 
 // wait until at most `ahead` slots (PER loads each) of this wave are still in flight
@@ -1573,19 +1612,46 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   uint8_t* ring = smem + w * (STG * R::kSlot);
   const int ring_pairs = it.nctx >> 1;  // pairs of two context pages
   const int mine = ring_pairs > w ? (ring_pairs - w + NW - 1) / NW : 0;
+  // Lane-only parts of the ring loads, the same for every slot: the byte offset of this lane's 16
+  // bytes inside its source page or plane, and which page or plane that is (KRing layouts).
+  const int o16 = 16 * lane;
+  // (codes: load i covers LDS bytes 1024 i .. 1024 i + 1023 of the interleaved pages)
+  // (the page is bit 7 of the LDS byte in both layouts, so one flag serves every code load)
+  int lpg;
+  const uint32_t kc_off = R::kcode_src(o16, &lpg), vc_off = R::vcode_src(o16, &lpg);
+  uint32_t kc_off1 = 0, vc_off1 = 0;
+  if constexpr (2 * R::kCodes > 1024) {
+    static_assert(R::kCodes == 1024, "one load per page's worth of codes");
+    kc_off1 = R::kcode_src(1024 + o16, &lpg);
+    vc_off1 = R::vcode_src(1024 + o16, &lpg);
+  }
+  const int pr_src = o16 < R::kKsz ? 0 : o16 < R::kKsz + R::kVsz ? 1 : 2;  // key planes, even, odd page
+  const uint32_t pr_off = pr_src == 0 ? o16 : pr_src == 1 ? o16 - R::kKsz : o16 - R::kKsz - R::kVsz;
   auto issue = [&](int k, int id0, int id1) {
     uint8_t* slot = ring + (k % STG) * R::kSlot;
     const int64_t u0 = unit0 + (int64_t)(id0 < 0 ? 0 : id0) * a.Hkv;
     const int64_t u1 = unit0 + (int64_t)(id1 < 0 ? 0 : id1) * a.Hkv;
-    ring_pair<R::kCodes>(pl.k + u0 * R::kCodes, pl.k + u1 * R::kCodes, slot, lane);
-    ring_pair<R::kCodes>(pl.v + u0 * R::kCodes, pl.v + u1 * R::kCodes, slot + R::kOffV, lane);
+    const uint8_t* k0 = pl.k + u0 * R::kCodes;
+    const uint8_t* k1 = pl.k + u1 * R::kCodes;
+    const uint8_t* v0 = pl.v + u0 * R::kCodes;
+    const uint8_t* v1 = pl.v + u1 * R::kCodes;
+    if constexpr (2 * R::kCodes <= 1024) {
+      if (2 * R::kCodes == 1024 || o16 < 2 * R::kCodes) {
+        __builtin_amdgcn_global_load_lds((lpg ? k1 : k0) + kc_off, (lds_ptr_t)slot, 16, 0, kNontemporal);
+        __builtin_amdgcn_global_load_lds((lpg ? v1 : v0) + vc_off, (lds_ptr_t)(slot + R::kOffV), 16, 0, kNontemporal);
+      }
+    } else {
+      const uint8_t* kbase = lpg ? k1 : k0;
+      const uint8_t* vbase = lpg ? v1 : v0;
+      __builtin_amdgcn_global_load_lds(kbase + kc_off, (lds_ptr_t)slot, 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(kbase + kc_off1, (lds_ptr_t)(slot + 1024), 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(vbase + vc_off, (lds_ptr_t)(slot + R::kOffV), 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(vbase + vc_off1, (lds_ptr_t)(slot + R::kOffV + 1024), 16, 0, kNontemporal);
+    }
     // the group's key parameters and both pages' value parameters are contiguous in the slot:
     // one load, each lane fetching its 16 bytes from the plane they come from
-    const int o = 16 * lane;
-    const uint8_t* src = o < R::kKsz ? pl.ksz + u0 * R::kKsz + o
-                         : o < R::kKsz + R::kVsz ? pl.vsz + u0 * R::kVsz + (o - R::kKsz)
-                                                 : pl.vsz + u1 * R::kVsz + (o - R::kKsz - R::kVsz);
-    if (R::kParams == 1024 || o < R::kParams)
+    const uint8_t* src = (pr_src == 0 ? pl.ksz + u0 * R::kKsz : pl.vsz + (pr_src == 1 ? u0 : u1) * R::kVsz) + pr_off;
+    if (R::kParams == 1024 || o16 < R::kParams)
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(slot + R::kOffKsz), 16, 0, kNontemporal);
   };
   auto pair_ids = [&](int k, int& id0, int& id1) {
@@ -1636,10 +1702,26 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int tk = 8 * ((n >> 2) & 1) + 4 * b + (n & 3);
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(slot + (n >> 3) * R::kCodes + tk * (D * BITS / 8)) + kg * KW;
+      constexpr int LB = 4 * KW;  // bytes of a row this lane reads: one LDS read of that width
+      const int ob = kg * LB;
+      // rows 4 b on are kKeyStepB further; the offset is kept opaque so that the two 8-byte reads of
+      // 2-bit codes are not fused into one paired read, whose two halves, 256 bytes apart, would
+      // share banks
+      uint32_t kstep = b * R::kKeyStepB;
+      if (b) asm volatile("" : "+v"(kstep));
+      const uint8_t* kp = slot + R::kcode_pos(n >> 3, tk - 4 * b, ob >> 4) + kstep + (ob & 15);
       uint32_t words[KW];
+      if constexpr (KW == 4) {
+        const u32x4 v = ld16(kp);
 #pragma unroll
-      for (int i = 0; i < KW; ++i) words[i] = kw[i];
+        for (int i = 0; i < 4; ++i) words[i] = v[i];
+      } else if constexpr (KW == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(kp);
+        words[0] = v[0];
+        words[1] = v[1];
+      } else {
+        words[0] = *reinterpret_cast<const uint32_t*>(kp);
+      }
       s_acc[b] = kb;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -1699,7 +1781,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     const u32x4 p16 = {ph[0], ph[1], ph[2], ph[3]};
     // ---- value side: P'_g = p * scale_t,g; bias_g += sum_t (z_t,g p_t - off_t P'_t,g)
     const uint16_t* vsz = reinterpret_cast<const uint16_t*>(slot + R::kOffVsz + vpage * R::kVsz) + vtok0;
-    const uint8_t* vcodes = slot + R::kOffV + vpage * R::kCodes;
+    const uint8_t* vcodes = slot + R::kOffV;
 #pragma unroll
     for (int gq = 0; gq < NGQ; ++gq) {
       u32x4 vs = ld16(vsz + (2 * gq) * kBlock);
@@ -1717,7 +1799,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       for (int h2 = 0; h2 < 2; ++h2) {
         const int db = 2 * gq + h2;
         const int dd = 16 * db + n;
-        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vcodes + dd * (kBlock * BITS / 8));
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vcodes + R::vcode_pos(vpage, dd * R::kVRow));
         // the lane's tokens vtok0 .. vtok0 + 7 of channel dd
         const u32x4 av = BITS == 2 ? ex.bits2(vw[0], kg & 1) : ex.bits4(vw[kg & 1]);
         acc_o[db] = mfma16<true>(av, pv, acc_o[db]);
