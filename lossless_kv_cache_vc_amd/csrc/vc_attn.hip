@@ -244,8 +244,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Cache policy of the ring loads: nontemporal ("nt").  K/V pages are read exactly once, and
 // streaming them without it leaves chip-wide HBM throughput near 6.3 TB/s instead of about
-// 7.2 TB/s on an MI355X.
+// 7.2 TB/s on an MI355X.  The exception is a verifying request cut into several row groups,
+// whose items all read the same K/V: those loads keep the default policy, so the lines stay in
+// L2 for the sibling items (placed on the same XCD; see decode_item).
 constexpr int kNontemporal = 2;
+constexpr int kTemporal = 0;
 
 // wait until at most N (< 64) of this wave's vector memory loads are outstanding (loads
 // complete in issue order).  gfx9 s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] and
@@ -335,6 +338,7 @@ struct VerifyState {
   int ps;                 // page of every tile this wave loads
   bool kwave;             // loads keys (waves 0-3) or values (4-7)
   bool wave_on;           // the wave's row block holds rows
+  bool shared_kv;         // other items (row groups) read the same K/V: loads keep lines in L2
   int kh, n, h, qpos;
   uint32_t lane_off[NL];  // byte offsets inside a page of this lane's loads
   uint32_t koff[NS];      // LDS offsets (inside a key stage) of this lane's score operands
@@ -372,10 +376,18 @@ __device__ __forceinline__ void verify_issue(const AttnArgs& a, const ItemCtx& i
   const uint8_t* page = vs.kwave ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip, unit)
                                  : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip, unit);
   uint8_t* dst = smem + (vs.kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;  // stage < 4 (K) or < 5 (V)
+  if (vs.shared_kv) {  // wave-uniform
 #pragma unroll
-  for (int i = 0; i < R::kLoads; ++i) {
-    const void* src = page + vs.lane_off[i];
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, kNontemporal);
+    for (int i = 0; i < R::kLoads; ++i) {
+      const void* src = page + vs.lane_off[i];
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, kTemporal);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R::kLoads; ++i) {
+      const void* src = page + vs.lane_off[i];
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, kNontemporal);
+    }
   }
 }
 
@@ -652,6 +664,7 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
   vs.kwave = w < 4;
   vs.ps = w & 3;
   vs.wave_on = rg * 128 + 32 * rb < it.rows_total;
+  vs.shared_kv = it.rq.nrg > 1;
   int32_t* units = reinterpret_cast<int32_t*>(smem + R::kIds);
   verify_begin<D>(a, it, row, vs, units, kVThreads);
   const int ntiles = vs.ntiles;
@@ -911,6 +924,7 @@ __device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, u
   vs.n = n;
   vs.h = h;
   vs.wave_on = rows0 < it.rows_total;
+  vs.shared_kv = false;  // the wide ring loads (wide_issue) always stream
   int32_t* units = reinterpret_cast<int32_t*>(smem + R::kIds);
   verify_begin<D>(a, it, row, vs, units, 64 * nw);
   const int ntiles = vs.ntiles;
