@@ -170,9 +170,9 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   std::vector<char> pool_used(npools, 0);
   const int vwaves = plan_vwaves(G, nreq, reqs);
   const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs, vwaves);
-  int64_t items = 0, part = 0, merge = 0;
   plan->any_split = 0;
   table->assign(nreq, ReqDev{});
+  std::vector<double> item_cost(nreq, 0.0);
   for (int i = 0; i < nreq; ++i) {
     const vc_req& r = reqs[i];
     char buf[200];
@@ -220,6 +220,28 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
     const int target = std::min(chunk, kMaxChunkPages);
     d.chunk_pages = split_context(pages, target, &d.nsplit);
     d.nrg = (int32_t)row_groups(r, G, vwaves);
+    // bytes one of the request's items streams: its pages times the bytes of a page of its pool
+    // (bf16 K and V, or 2/4-bit codes with their scales and zeros)
+    const double page_bytes = p.bits == 16 ? 64.0 * D : (p.bits == 2 ? 12.0 : 20.0) * D;
+    item_cost[i] = std::min(pages, d.chunk_pages) * page_bytes;
+  }
+  // Item numbering follows the table order.  In a ragged batch that mixes drafting and verifying
+  // requests the table lists requests by decreasing cost per item, so the most expensive items
+  // are dispatched first and the launch does not end on a tail of long items (longest processing
+  // time first); other launches keep the caller's order.  Nothing outside the plan depends on the
+  // order: each entry carries its request's own slot, rows and page-table row.
+  std::vector<int> order(nreq);
+  for (int i = 0; i < nreq; ++i) order[i] = i;
+  if (is_mixed(nreq, reqs))
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return item_cost[x] > item_cost[y]; });
+  {
+    std::vector<ReqDev> sorted(nreq);
+    for (int j = 0; j < nreq; ++j) sorted[j] = (*table)[order[j]];
+    table->swap(sorted);
+  }
+  int64_t items = 0, part = 0, merge = 0;
+  for (int j = 0; j < nreq; ++j) {
+    ReqDev& d = (*table)[j];
     d.item_base = (int32_t)items;
     items += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * d.nrg;
     // merge work-groups are counted for every request (a request without splits owns none), so
@@ -227,14 +249,15 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
     d.merge_base = (int32_t)std::min<int64_t>(merge, INT32_MAX);
     if (d.nsplit > 1) {
       d.part_base = part;
-      part += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * r.rows * G * (D + 4);
-      const int64_t rows = (int64_t)s->num_layers * s->num_kv_heads * r.rows * G;
+      part += (int64_t)s->num_layers * s->num_kv_heads * d.nsplit * d.rows * G * (D + 4);
+      const int64_t rows = (int64_t)s->num_layers * s->num_kv_heads * d.rows * G;
       const int rpg = merge_rows_per_group(D);
       merge += (rows + rpg - 1) / rpg;
       plan->any_split = 1;
     } else {
       d.part_base = -1;
     }
+    if (items > (1LL << 30)) return fail(VC_EINVAL, "too many work items");
   }
   if (items > (1LL << 30)) return fail(VC_EINVAL, "too many work items");
   if (merge > (1LL << 30)) return fail(VC_EINVAL, "too many split rows");
