@@ -422,7 +422,9 @@ def measure_config(name, steps, warmup, cpu_budget, staged=False, temperature=0.
     print(f"# built {cfg.name} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
     rec = {"workload": f"{cfg.name}: {cfg.note}"}
     if cfg.mixed:
-        rec.update(mixed_record(cfg, wl, steps, warmup))
+        # one mixed launch is under a millisecond: time at least 20 of them after 5 warm-ups,
+        # so that the entry does not rest on a few launches at a cold clock
+        rec.update(mixed_record(cfg, wl, max(steps, 20), max(warmup, 5)))
         wl.logits()
         rec.update(logits_evidence(cfg, wl))
         round_bytes = rec["bytes"]["launch"]
