@@ -1,0 +1,66 @@
+"""Seeded random shapes through the draft and verify launches, against the oracle.
+
+Twelve configurations drawn once from a fixed seed: query-head grouping G in {1, 2, 4, 8, 16},
+d in {64, 128}, one or two layer slices, one to three requests with ragged contexts of 1 to 700
+tokens (every fourth case opens with one of at most 16), drafted blocks of up to 64 rows (so
+verify launches reach the wide work-groups and several row groups), one compression kind per
+configuration, and context splits of 0, 4 or 8 pages.  Every draft step and every verify row is
+compared with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_close, require_gpu, tight_tol
+from oracle import workload as ow
+from vcsynth import configs as C
+
+pytestmark = pytest.mark.gpu
+
+COMPS = [C.COMP_DROP, C.COMP_KIVI2, C.COMP_DROP_KIVI4]
+
+
+def _draw(k):
+    rs = np.random.RandomState(20261203 + 7919 * k)
+    G = int(rs.choice([1, 2, 4, 8, 16]))
+    d = int(rs.choice([64, 128]))
+    Hkv = int(rs.choice([1, 2]))
+    L = int(rs.randint(1, 3))
+    comp = COMPS[k % 3]
+    x = int(rs.randint(1, 65))
+    reqs = []
+    for i in range(int(rs.randint(1, 4))):
+        # every fourth case starts with a context of at most one partial page
+        n = int(rs.randint(1, 17)) if (k % 4 == 3 and i == 0) else int(rs.randint(1, 701))
+        if comp == C.COMP_KIVI2:
+            reqs.append(C.Request(ctx_len=n, x=x, comp=comp))
+        else:
+            reqs.append(C.Request(ctx_len=n, x=x, comp=comp, recent=min(n, 32), top=n // 4))
+    split = int(rs.choice([0, 4, 8]))
+    cfg = C.Config(f"random{k}", 100 + k, L=L, Hq=G * Hkv, Hkv=Hkv, d=d, reqs=reqs,
+                   wu_width=G * Hkv * d, vocab=1024)
+    return cfg, split
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_shape_parity(k):
+    require_gpu()
+    from lossless_kv_cache_vc_amd.harness import Workload
+    cfg, split = _draw(k)
+    desc = (f"case {k}: G={cfg.G} d={cfg.d} Hkv={cfg.Hkv} L={cfg.L} comp={cfg.reqs[0].comp} "
+            f"x={cfg.reqs[0].x} n={[r.ctx_len for r in cfg.reqs]} split_pages={split}")
+    print(desc, flush=True)
+    wl = Workload(cfg)
+    for i in range(max(r.x for r in cfg.reqs)):
+        wl.run_draft(i, split)
+    wl.run_verify(split)
+    torch.cuda.synchronize()
+    for r, req in enumerate(cfg.reqs):
+        for l in range(cfg.L):
+            cc = [ow.compressed(cfg, r, l, g) for g in range(cfg.Hkv)]
+            want = ow.draft_out(cfg, r, l, range(req.x), comp_cache=cc)
+            got = wl.out_d[r, l, :req.x].double().cpu().numpy()
+            assert_close(got, want, tight_tol(req.kept, kivi=req.bits != 16), f"{desc} draft r={r} l={l}")
+            want = ow.verify_out(cfg, r, l)
+            got = wl.out_v[r, l, :req.x].double().cpu().numpy()
+            assert_close(got, want, tight_tol(req.ctx_len), f"{desc} verify r={r} l={l}")
