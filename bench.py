@@ -34,6 +34,11 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 METRIC = "verify+draft attention achieved HBM TB/s (% of peak), Llama-3.1-8B shape 32K"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# per-workload lines (not the headline, which keeps exactly --warmup and --steps): warm up for at
+# least WARM_S seconds and time at least MIN_TIMED_S seconds, so that sub-millisecond steps are
+# timed at the steady clock
+WARM_S = 0.25
+MIN_TIMED_S = 0.15
 TIE_GAP = 1e-3  # a logits row whose top-2 gap is below this is a near-tie (flagged)
 
 
@@ -254,9 +259,33 @@ def logits_evidence(cfg, wl):
     return out
 
 
-def time_round(cfg, wl, steps, warmup, temperature=0.0):
-    """Warm-up rounds, then `steps` timed rounds; per-phase milliseconds from HIP events on the
-    stream the kernels run on."""
+def warm_up(step, warmup, warm_s):
+    """`warmup` untimed steps, then more until `warm_s` seconds of wall time have passed; returns
+    (steps run, wall seconds per step).  After an idle gap the GPU clock climbs for some tens of
+    milliseconds, so a workload whose step is a fraction of a millisecond, timed right after a
+    couple of warm-up steps, reads the climb rather than the steady rate."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or (warm_s > 0 and time.perf_counter() - t0 < warm_s):
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()  # keep the host within a few steps of the GPU
+    torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) / max(n, 1)
+
+
+def timed_steps(steps, per_step_s, min_timed_s, cap=4000):
+    """At least `steps`, and enough that the timed region spans `min_timed_s` seconds."""
+    if min_timed_s <= 0 or per_step_s <= 0:
+        return steps
+    return max(steps, min(cap, int(min_timed_s / per_step_s) + 1))
+
+
+def time_round(cfg, wl, steps, warmup, temperature=0.0, warm_s=0.0, min_timed_s=0.0):
+    """Warm-up rounds, then `steps` timed rounds (more with `min_timed_s`); per-phase
+    milliseconds from HIP events on the stream the kernels run on."""
     import torch
     x = max(r.x for r in cfg.reqs)
 
@@ -272,9 +301,9 @@ def time_round(cfg, wl, steps, warmup, temperature=0.0):
         wl.accept(temperature)
         evs[4].record()
 
-    for _ in range(warmup):
-        one_round([torch.cuda.Event(enable_timing=True) for _ in range(5)])
-    torch.cuda.synchronize()
+    warmed, per_round = warm_up(lambda: one_round([torch.cuda.Event(enable_timing=True) for _ in range(5)]),
+                                warmup, warm_s)
+    steps = timed_steps(steps, per_round, min_timed_s)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -284,7 +313,7 @@ def time_round(cfg, wl, steps, warmup, temperature=0.0):
     wall = time.perf_counter() - t0
     ms = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / steps
     return {"draft": ms(0, 1), "verify": ms(1, 2), "logits": ms(2, 3), "accept": ms(3, 4),
-            "wall_ms_per_step": wall * 1e3 / steps}
+            "wall_ms_per_step": wall * 1e3 / steps, "steps": steps, "warmup": warmed}
 
 
 def round_record(cfg, wl, t, steps, warmup):
@@ -386,12 +415,11 @@ def staged_round(cfg, wl, steps, draft_ms_alone=None):
             "note": "full pool cleared first; the verify reads only staged bytes"}
 
 
-def mixed_record(cfg, wl, steps, warmup):
+def mixed_record(cfg, wl, steps, warmup, warm_s=0.0, min_timed_s=0.0):
     import torch
     nbytes = wl.mixed_bytes()
-    for _ in range(warmup):
-        wl.run_mixed()
-    torch.cuda.synchronize()
+    warmup, per_launch = warm_up(wl.run_mixed, warmup, warm_s)
+    steps = timed_steps(steps, per_launch, min_timed_s)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
     ev[0].record()
@@ -422,15 +450,13 @@ def measure_config(name, steps, warmup, cpu_budget, staged=False, temperature=0.
     print(f"# built {cfg.name} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
     rec = {"workload": f"{cfg.name}: {cfg.note}"}
     if cfg.mixed:
-        # one mixed launch is under a millisecond: time at least 20 of them after 5 warm-ups,
-        # so that the entry does not rest on a few launches at a cold clock
-        rec.update(mixed_record(cfg, wl, max(steps, 20), max(warmup, 5)))
+        rec.update(mixed_record(cfg, wl, steps, warmup, warm_s=WARM_S, min_timed_s=MIN_TIMED_S))
         wl.logits()
         rec.update(logits_evidence(cfg, wl))
         round_bytes = rec["bytes"]["launch"]
     else:
-        t = time_round(cfg, wl, steps, warmup, temperature)
-        rec.update(round_record(cfg, wl, t, steps, warmup))
+        t = time_round(cfg, wl, steps, warmup, temperature, warm_s=WARM_S, min_timed_s=MIN_TIMED_S)
+        rec.update(round_record(cfg, wl, t, t["steps"], t["warmup"]))
         rec.update(logits_evidence(cfg, wl))
         round_bytes = rec["bytes"]["round"]
     if cpu_budget > 0:

@@ -29,3 +29,10 @@ def test_host_info_names_the_host():
     h = bench.host_info()
     assert set(h) == {"cpu_model", "logical_cpus", "ram_gib"}
     assert h["logical_cpus"] >= 1
+
+
+def test_short_steps_are_timed_over_a_minimum_span():
+    assert bench.timed_steps(3, 0.06, 0.15) == 3                 # 60 ms rounds: the count holds
+    assert bench.timed_steps(3, 0.0008, 0.15) == 188             # 0.8 ms launches: 0.15 s of them
+    assert bench.timed_steps(3, 1e-6, 0.15) == 4000              # capped
+    assert bench.timed_steps(10, 0.0008, 0.0) == 10              # the headline keeps --steps
