@@ -91,6 +91,9 @@ typedef struct {
  *         (odd pages' entries unused)
  *   v_sz  fp16 [L][nb][Hkv][d/32][2][16]   per 32-channel group: the scales of the page's 16
  *         tokens, then their zeros
+ * Limits: L*nb*Hkv below 2^31; in a KIVI pool also nb*Hkv*max(16*d*bits/8, 4*d) bytes (one layer
+ * of the largest per-page array) below 2^32.  A launch naming a pool past them fails with
+ * VC_EUNSUPPORTED before anything is enqueued.
  */
 typedef struct {
   int32_t bits;                /* 16, 2 or 4 */

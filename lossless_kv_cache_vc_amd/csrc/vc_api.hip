@@ -92,7 +92,14 @@ static int check_pool(const vc_pool* p, int head_dim, int num_layers, int num_kv
     snprintf(buf, sizeof buf, "%s pool: layers x blocks x kv heads must be below 2^31", name);
     return fail(VC_EUNSUPPORTED, buf);
   }
-  (void)head_dim;
+  // the KIVI draft ring addresses a pool's pages of one (layer, kv head) with 32-bit byte offsets
+  if (p->bits != 16) {
+    const int64_t page_bytes = std::max<int64_t>((int64_t)kBlock * head_dim * p->bits / 8, 4LL * head_dim);
+    if ((int64_t)p->num_blocks * num_kv_heads * page_bytes >= (1LL << 32)) {
+      snprintf(buf, sizeof buf, "%s pool: blocks x kv heads x page code bytes must be below 2^32", name);
+      return fail(VC_EUNSUPPORTED, buf);
+    }
+  }
   return VC_OK;
 }
 

@@ -1641,32 +1641,42 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   }
   const int pr_src = o16 < R::kKsz ? 0 : o16 < R::kKsz + R::kVsz ? 1 : 2;  // key planes, even, odd page
   const uint32_t pr_off = pr_src == 0 ? o16 : pr_src == 1 ? o16 - R::kKsz : o16 - R::kKsz - R::kVsz;
+  // Each load has a scalar base (the pool at this layer and kv head) and a 32-bit per-lane offset
+  // (block id x kv heads x page bytes, plus the lane's offset in the page; the host keeps a KIVI
+  // pool's blocks x kv heads x page bytes below 2^32).  A lane's choice between the pair's two
+  // pages is a mask fixed for the item, so a pair's addresses cost a few integer instructions.
+  const uint8_t* kbase = pl.k + unit0 * R::kCodes;
+  const uint8_t* vbase = pl.v + unit0 * R::kCodes;
+  // (the parameter planes come from two pools: a per-lane base, fixed for the item)
+  const uint8_t* pbase = (pr_src == 0 ? pl.ksz + unit0 * R::kKsz : pl.vsz + unit0 * R::kVsz) + pr_off;
+  // lane masks, kept in vector registers (the empty asm statements emit nothing) so that each
+  // selection is one and / and-or with the scalar operand
+  uint32_t csel = lpg ? ~0u : 0u;  // lanes fetching the odd page's codes
+  uint32_t pselk = pr_src == 0 ? ~0u : 0u, psel0 = pr_src == 1 ? ~0u : 0u, psel1 = pr_src == 2 ? ~0u : 0u;
+  asm volatile("" : "+v"(csel), "+v"(pselk), "+v"(psel0), "+v"(psel1));
+  const uint32_t cstride = (uint32_t)a.Hkv * R::kCodes;
+  const uint32_t kpstride = (uint32_t)a.Hkv * R::kKsz, vpstride = (uint32_t)a.Hkv * R::kVsz;
   auto issue = [&](int k, int id0, int id1) {
     uint8_t* slot = ring + (k % STG) * R::kSlot;
-    const int64_t u0 = unit0 + (int64_t)(id0 < 0 ? 0 : id0) * a.Hkv;
-    const int64_t u1 = unit0 + (int64_t)(id1 < 0 ? 0 : id1) * a.Hkv;
-    const uint8_t* k0 = pl.k + u0 * R::kCodes;
-    const uint8_t* k1 = pl.k + u1 * R::kCodes;
-    const uint8_t* v0 = pl.v + u0 * R::kCodes;
-    const uint8_t* v1 = pl.v + u1 * R::kCodes;
+    const uint32_t i0 = id0 < 0 ? 0u : (uint32_t)id0, i1 = id1 < 0 ? 0u : (uint32_t)id1;
+    // (the differences wrap in 32 bits; every sum stays below 2^32)
+    const uint32_t co = i0 * cstride + (csel & ((i1 - i0) * cstride));
     if constexpr (2 * R::kCodes <= 1024) {
       if (2 * R::kCodes == 1024 || o16 < 2 * R::kCodes) {
-        __builtin_amdgcn_global_load_lds((lpg ? k1 : k0) + kc_off, (lds_ptr_t)slot, 16, 0, kNontemporal);
-        __builtin_amdgcn_global_load_lds((lpg ? v1 : v0) + vc_off, (lds_ptr_t)(slot + R::kOffV), 16, 0, kNontemporal);
+        __builtin_amdgcn_global_load_lds(kbase + (co + kc_off), (lds_ptr_t)slot, 16, 0, kNontemporal);
+        __builtin_amdgcn_global_load_lds(vbase + (co + vc_off), (lds_ptr_t)(slot + R::kOffV), 16, 0, kNontemporal);
       }
     } else {
-      const uint8_t* kbase = lpg ? k1 : k0;
-      const uint8_t* vbase = lpg ? v1 : v0;
-      __builtin_amdgcn_global_load_lds(kbase + kc_off, (lds_ptr_t)slot, 16, 0, kNontemporal);
-      __builtin_amdgcn_global_load_lds(kbase + kc_off1, (lds_ptr_t)(slot + 1024), 16, 0, kNontemporal);
-      __builtin_amdgcn_global_load_lds(vbase + vc_off, (lds_ptr_t)(slot + R::kOffV), 16, 0, kNontemporal);
-      __builtin_amdgcn_global_load_lds(vbase + vc_off1, (lds_ptr_t)(slot + R::kOffV + 1024), 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(kbase + (co + kc_off), (lds_ptr_t)slot, 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(kbase + (co + kc_off1), (lds_ptr_t)(slot + 1024), 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(vbase + (co + vc_off), (lds_ptr_t)(slot + R::kOffV), 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(vbase + (co + vc_off1), (lds_ptr_t)(slot + R::kOffV + 1024), 16, 0, kNontemporal);
     }
     // the group's key parameters and both pages' value parameters are contiguous in the slot:
     // one load, each lane fetching its 16 bytes from the plane they come from
-    const uint8_t* src = (pr_src == 0 ? pl.ksz + u0 * R::kKsz : pl.vsz + (pr_src == 1 ? u0 : u1) * R::kVsz) + pr_off;
+    const uint32_t po = (pselk & (i0 * kpstride)) | (psel0 & (i0 * vpstride)) | (psel1 & (i1 * vpstride));
     if (R::kParams == 1024 || o16 < R::kParams)
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(slot + R::kOffKsz), 16, 0, kNontemporal);
+      __builtin_amdgcn_global_load_lds(pbase + po, (lds_ptr_t)(slot + R::kOffKsz), 16, 0, kNontemporal);
   };
   auto pair_ids = [&](int k, int& id0, int& id1) {
     const int pp = w + NW * k;

@@ -75,6 +75,12 @@ def test_host_validation_rejects_bad_arguments():
     _expect(vc.VC_EINVAL, lambda: vc.draft_attn(_shape(Hq=32, Hkv=2), [vc.Req(0, 0, 10, 0, 0, 2, 1)],
                                                  t, t, t, _pool(), t, None, 0, 0))  # rows*G > 16
     _expect(vc.VC_EINVAL, lambda: vc.verify_attn(_shape(), [ok_req], t, t, t, _pool(), t, None, 6, 0))
+    # a KIVI pool whose one layer of 512-byte page arrays reaches 2^32 bytes (2^22 blocks x 2 kv
+    # heads x 512 B) is refused; L x blocks x kv heads (2^24) is within its own limit
+    big = _pool(bits=2)
+    big.num_blocks = 1 << 22
+    draft_req = vc.Req(0, 0, 100, 0, 0, 1, vc.VC_DRAFT)
+    _expect(vc.VC_EUNSUPPORTED, lambda: vc.draft_attn(_shape(), [draft_req], t, t, t, big, t, None, 0, 0))
     # splitting needs a workspace
     _expect(vc.VC_ENOSPACE, lambda: vc.verify_attn(_shape(), [vc.Req(0, 0, 120, 0, 0, 8, 0)], t, t, t,
                                                    _pool(), t, None, 4, 0))
