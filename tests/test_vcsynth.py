@@ -50,6 +50,20 @@ def test_normal_table_is_rounded_inverse_cdf(sigma):
     assert np.array_equal(got.astype(np.uint32), want_bits.astype(np.uint32))
 
 
+@pytest.mark.parametrize("sigma", [1.0, 1 / 64.0])
+def test_bucketed_lookup_equals_the_threshold_search(sigma):
+    """The per-bucket shortcut gives #{thresholds <= u} exactly: random u, every threshold and
+    its neighbours, bucket edges, and the ends of the range."""
+    t = normal_table(sigma)
+    th = t.thresholds.astype(np.int64)
+    edges = np.arange(0, 1 << 32, 1 << 12, dtype=np.int64)
+    u = np.concatenate([rng.u32(3, 4, np.arange(200000)).astype(np.int64), th - 1, th, th + 1,
+                        edges, edges - 1, [0, (1 << 32) - 1]])
+    u = np.clip(u, 0, (1 << 32) - 1).astype(np.uint32)
+    assert np.array_equal(rng.bucket_of(t, u), np.searchsorted(t.thresholds, u, side="right"))
+    assert rng.normal_bf16_bits(3, 4, 5, t).shape == ()  # scalar index, scalar result
+
+
 def test_normal_moments_and_ks():
     t = normal_table(1.0)
     x = rng.bf16_bits_to_f64(rng.normal_bf16_bits(11, 2, np.arange(400000), t))

@@ -78,11 +78,43 @@ def uniform01(seed: int, stream: int, idx) -> np.ndarray:
     return (u32(seed, stream, idx).astype(np.float64) + 0.5) / 4294967296.0
 
 
+_BUCKET_BITS = 20
+_buckets = {}
+
+
+def _bucket_bounds(table):
+    """For each of the 2**20 buckets of the top bits of u, the bucket index ``#{thresholds <= u}``
+    at the bucket's first and last u.  The count is monotone in u, so where the two agree every
+    u of the bucket has that index."""
+    hit = _buckets.get(id(table))
+    if hit is not None and hit[0] is table:
+        return hit[1], hit[2]
+    first = np.arange(1 << _BUCKET_BITS, dtype=np.uint64) << np.uint64(32 - _BUCKET_BITS)
+    last = first + np.uint64((1 << (32 - _BUCKET_BITS)) - 1)
+    th = table.thresholds.astype(np.uint64)
+    lo = np.searchsorted(th, first, side="right").astype(np.int32)
+    hi = np.searchsorted(th, last, side="right").astype(np.int32)
+    _buckets[id(table)] = (table, lo, hi)
+    return lo, hi
+
+
 def normal_bf16_bits(seed: int, stream: int, idx, table) -> np.ndarray:
-    """bf16 bit patterns (uint16) of N(0, sigma^2) draws, sigma fixed by ``table``."""
-    u = u32(seed, stream, idx)
-    k = np.searchsorted(table.thresholds, u, side="right")
-    return table.values_bits[k]
+    """bf16 bit patterns (uint16) of N(0, sigma^2) draws, sigma fixed by ``table``: the value of
+    bucket ``#{thresholds <= u}``.  The count is read from a per-bucket table of the top bits of
+    u, and searched among the thresholds only where a bucket holds one."""
+    u = np.asarray(u32(seed, stream, idx))
+    return table.values_bits[bucket_of(table, u.reshape(-1))].reshape(u.shape)
+
+
+def bucket_of(table, u: np.ndarray) -> np.ndarray:
+    """``#{thresholds <= u}`` for a 1-D uint32 array u (the same as a right-sided search)."""
+    lo, hi = _bucket_bounds(table)
+    b = u >> np.uint32(32 - _BUCKET_BITS)
+    k = lo[b]
+    amb = hi[b] != k
+    if amb.any():
+        k[amb] = np.searchsorted(table.thresholds, u[amb], side="right")
+    return k
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
