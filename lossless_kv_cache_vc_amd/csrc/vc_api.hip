@@ -178,6 +178,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   const int vwaves = plan_vwaves(G, nreq, reqs);
   const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs, vwaves);
   plan->any_split = 0;
+  plan->has_verify = plan->has_draft = 0;
   table->assign(nreq, ReqDev{});
   std::vector<double> item_cost(nreq, 0.0);
   for (int i = 0; i < nreq; ++i) {
@@ -216,6 +217,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
                p.max_pages);
       return fail(VC_EINVAL, buf);
     }
+    (r.kind == VC_VERIFY ? plan->has_verify : plan->has_draft) = 1;
     ReqDev& d = (*table)[i];
     d.slot = r.slot;
     d.pool = r.pool;

@@ -2082,8 +2082,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
 int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_t stream) {
   if (plan.nitems == 0) return VC_OK;
   const dim3 grid(args.nitems_pad);
-  bool has_v = false, has_d = false;
-  for (int i = 0; i < args.nreq; ++i) (args.reqs[i].kind == VC_VERIFY ? has_v : has_d) = true;
+  // (args.reqs holds only the first kInlineReqs requests: the kinds come from the plan)
+  const bool has_v = plan.has_verify, has_d = plan.has_draft;
   if (args.vwaves) {
     // verify-only launches; the kernel deals the 8 ring slots of a tile over its waves, at most
     // two per wave

@@ -103,6 +103,8 @@ struct Plan {
   int64_t part_floats = 0;
   int any_split = 0;
   int head_dim = 0;
+  int has_verify = 0;  // the launch holds verifying / drafting requests (over all of them, not
+  int has_draft = 0;   // only the ones the kernel arguments carry)
 };
 int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const vc_pool* pools,
               int split_pages, AttnArgs* args, Plan* plan, std::vector<ReqDev>* table);
