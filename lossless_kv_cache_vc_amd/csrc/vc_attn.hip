@@ -36,7 +36,14 @@ constexpr int kDWaves = 4;            // waves of a draft-only work-group (bf16 
 constexpr int kDThreads = 64 * kDWaves;
 constexpr int kKWaves = 12;           // waves of a draft-only work-group (KIVI caches): three per SIMD
 constexpr int kKThreads = 64 * kKWaves;
-constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
+// Headroom (log2 units) a row's maximum may gain before the running maximum is moved and the
+// accumulators rescaled.  Where the weights enter the value product as bf16 (8 significant bits)
+// the running maximum moves whenever it grows: the key that sets it then has weight exactly 1,
+// which bf16 holds exactly.  With headroom, a key that dominates its row would have its weight
+// rounded by up to 2^-8 relative, an output error of up to 2^-8 |v| (over 5e-3 for rows with one
+// dominant key of a short context).  fp16 weights (11 bits) keep 8 units of headroom.
+constexpr float kRescaleBf16 = 0.0f;
+constexpr float kRescaleF16 = 8.0f;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ bf16x8 as_bf(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -438,7 +445,7 @@ __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>
   mloc = half_swap_max(mloc);
   const float sc = vs.sc;
   const float m_new = fmaxf(vs.m_run, mloc * sc);
-  if (__any(m_new > vs.m_run + kLazyRescale)) {
+  if (__any(m_new > vs.m_run + kRescaleBf16)) {
     const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
     vs.l_run *= alpha;
 #pragma unroll
@@ -494,7 +501,7 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
   mloc = half_swap_max(mloc);
   const float sc = vs.sc;
   const float m_new = fmaxf(vs.m_run, mloc * sc);
-  if (__any(m_new > vs.m_run + kLazyRescale)) {
+  if (__any(m_new > vs.m_run + kRescaleBf16)) {
     const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
     vs.l_run *= alpha;
 #pragma unroll
@@ -1208,7 +1215,7 @@ __device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     mloc = wave_xor_max(mloc, 16);
     mloc = wave_xor_max(mloc, 32);
     const float m_new = fmaxf(m_run, mloc * sc);
-    if (__any(m_new > m_run + kLazyRescale)) {
+    if (__any(m_new > m_run + kRescaleBf16)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -1343,7 +1350,7 @@ __device__ __forceinline__ void draft_pair_generic(const AttnArgs& a, const Item
   mloc = wave_xor_max(mloc, 16);
   mloc = wave_xor_max(mloc, 32);
   const float m_new = fmaxf(m_run, mloc * sc);
-  if (__any(m_new > m_run + kLazyRescale)) {
+  if (__any(m_new > m_run + (KIVI ? kRescaleF16 : kRescaleBf16))) {
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
@@ -1784,7 +1791,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mloc = row_max4(mloc);
     const float m_new = fmaxf(m_run, mloc * sc);
-    if (__any(m_new > m_run + kLazyRescale)) {
+    if (__any(m_new > m_run + kRescaleF16)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll

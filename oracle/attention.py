@@ -18,10 +18,15 @@ from __future__ import annotations
 import numpy as np
 
 
-def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible=None) -> np.ndarray:
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible=None, spread: bool = False):
     """softmax(q k^T / sqrt(d)) v, rows restricted to ``visible`` keys (bool [rows][keys]).
 
-    Two passes: row maximum over visible scores, then normalised exponential weights."""
+    Two passes: row maximum over visible scores, then normalised exponential weights.
+
+    With ``spread``, also returns sqrt(sum_t (w_t v_tc)^2) per row and channel, w_t the
+    normalised weights.  This is not part of the method: it sizes the parity gates, since an
+    implementation whose weights carry independent relative rounding errors of standard deviation
+    sigma has an output error of standard deviation at most sigma times this spread."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -31,15 +36,19 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible=None) -> np.n
         s = np.where(visible, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     w = np.exp(s - m)
-    return (w @ v) / w.sum(axis=1, keepdims=True)
+    out = (w @ v) / w.sum(axis=1, keepdims=True)
+    if not spread:
+        return out
+    wn = w / w.sum(axis=1, keepdims=True)
+    return out, np.sqrt((wn * wn) @ (v * v))
 
 
 def verify_unit(q: np.ndarray, kctx: np.ndarray, vctx: np.ndarray,
-                kblk: np.ndarray, vblk: np.ndarray) -> np.ndarray:
+                kblk: np.ndarray, vblk: np.ndarray, spread: bool = False):
     """Verify pass of one (request, layer, kv-head).
 
     q: [x][G][d] (drafted rows x query heads of the group), kctx/vctx: [n][d] full context,
-    kblk/vblk: [>=x][d] drafted rows.  Returns [x][G][d]."""
+    kblk/vblk: [>=x][d] drafted rows.  Returns [x][G][d] (and its spread, see ``attention``)."""
     x, G, d = q.shape
     n = kctx.shape[0]
     keys = np.concatenate([kctx, kblk[:x]], axis=0)
@@ -47,19 +56,23 @@ def verify_unit(q: np.ndarray, kctx: np.ndarray, vctx: np.ndarray,
     row_tok = np.repeat(np.arange(x), G)                      # row (i, j) -> token i
     key_blk = np.arange(n + x) - n                            # <0: context, else block row
     visible = key_blk[None, :] <= row_tok[:, None]
+    if spread:
+        out, spr = attention(q.reshape(x * G, d), keys, vals, visible, spread=True)
+        return out.reshape(x, G, d), spr.reshape(x, G, d)
     out = attention(q.reshape(x * G, d), keys, vals, visible)
     return out.reshape(x, G, d)
 
 
 def draft_unit(q: np.ndarray, kcomp: np.ndarray, vcomp: np.ndarray,
-               kblk: np.ndarray, vblk: np.ndarray, step: int) -> np.ndarray:
+               kblk: np.ndarray, vblk: np.ndarray, step: int, spread: bool = False):
     """Draft step ``step`` of one (request, layer, kv-head): one query token, G heads.
 
     q: [G][d]; kcomp/vcomp: [k][d] compressed context (kept rows, or dequantised rows);
-    kblk/vblk: drafted rows, of which 0..step are visible.  Returns [G][d]."""
+    kblk/vblk: drafted rows, of which 0..step are visible.  Returns [G][d] (and its spread, see
+    ``attention``)."""
     keys = np.concatenate([kcomp, kblk[:step + 1]], axis=0)
     vals = np.concatenate([vcomp, vblk[:step + 1]], axis=0)
-    return attention(q, keys, vals)
+    return attention(q, keys, vals, spread=spread)
 
 
 def gqa_group(h: int, G: int) -> int:

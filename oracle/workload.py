@@ -76,35 +76,47 @@ def queries(cfg: C.Config, r: int, l: int, x: int) -> np.ndarray:
     return bf16_to_f64(T.q_bits(cfg, r, l, x))
 
 
-def verify_out(cfg: C.Config, r: int, l: int, g: Optional[int] = None, x: Optional[int] = None):
-    """Verify output [x][Hq][d] (or [x][G][d] for one kv head g)."""
+def verify_out(cfg: C.Config, r: int, l: int, g: Optional[int] = None, x: Optional[int] = None,
+               spread: bool = False):
+    """Verify output [x][Hq][d] (or [x][G][d] for one kv head g); with ``spread``, also the
+    weight spread of every output element (see ``attention.attention``)."""
     x = cfg.reqs[r].x if x is None else x
     q = queries(cfg, r, l, x)
     G = cfg.G
     heads = range(cfg.Hkv) if g is None else [g]
-    outs = []
+    outs, sprs = [], []
     for gg in heads:
         kc, vc = context(cfg, r, l, gg)
         kb, vb = block(cfg, r, l, gg, x)
-        outs.append(att.verify_unit(q[:, gg * G:(gg + 1) * G], kc, vc, kb, vb))
-    return np.concatenate(outs, axis=1)
+        res = att.verify_unit(q[:, gg * G:(gg + 1) * G], kc, vc, kb, vb, spread=spread)
+        outs.append(res[0] if spread else res)
+        if spread:
+            sprs.append(res[1])
+    out = np.concatenate(outs, axis=1)
+    return (out, np.concatenate(sprs, axis=1)) if spread else out
 
 
-def draft_out(cfg: C.Config, r: int, l: int, steps, g: Optional[int] = None, comp_cache=None):
-    """Draft outputs for the given steps: [len(steps)][Hq][d] (or [..][G][d] for kv head g)."""
+def draft_out(cfg: C.Config, r: int, l: int, steps, g: Optional[int] = None, comp_cache=None,
+              spread: bool = False):
+    """Draft outputs for the given steps: [len(steps)][Hq][d] (or [..][G][d] for kv head g);
+    with ``spread``, also the weight spread of every output element."""
     steps = list(steps)
     xmax = max(steps) + 1
     q = queries(cfg, r, l, xmax)
     G = cfg.G
     heads = range(cfg.Hkv) if g is None else [g]
     out = np.zeros((len(steps), G * len(heads), cfg.d))
+    spr = np.zeros_like(out)
     for hi, gg in enumerate(heads):
         cm = comp_cache[gg] if comp_cache is not None else compressed(cfg, r, l, gg)
         kb, vb = block(cfg, r, l, gg, xmax)
         for si, i in enumerate(steps):
-            out[si, hi * G:(hi + 1) * G] = att.draft_unit(q[i, gg * G:(gg + 1) * G], cm.k, cm.v,
-                                                        kb, vb, i)
-    return out
+            res = att.draft_unit(q[i, gg * G:(gg + 1) * G], cm.k, cm.v, kb, vb, i, spread=spread)
+            if spread:
+                out[si, hi * G:(hi + 1) * G], spr[si, hi * G:(hi + 1) * G] = res
+            else:
+                out[si, hi * G:(hi + 1) * G] = res
+    return (out, spr) if spread else out
 
 
 @dataclass
@@ -120,13 +132,20 @@ class RoundResult:
     accept_len: int
     next_tok: int
     flagged: bool
+    verify_spread: Optional[np.ndarray] = None   # weight spreads (``attention.attention``)
+    draft_spread: Optional[np.ndarray] = None
 
 
-def round_instance(cfg: C.Config, r: int, l: int) -> RoundResult:
+def round_instance(cfg: C.Config, r: int, l: int, spread: bool = False) -> RoundResult:
     """One draft-verify round of instance (r, l): x draft steps, verify, logits, accept."""
     x = cfg.reqs[r].x
-    vo = verify_out(cfg, r, l)
-    do = draft_out(cfg, r, l, range(x))
+    vs = ds = None
+    if spread:
+        vo, vs = verify_out(cfg, r, l, spread=True)
+        do, ds = draft_out(cfg, r, l, range(x), spread=True)
+    else:
+        vo = verify_out(cfg, r, l)
+        do = draft_out(cfg, r, l, range(x))
     wu = bf16_to_f64(T.wu_bits(cfg))
     zv = acc.logits(vo.reshape(x, -1), wu)
     zd = acc.logits(do.reshape(x, -1), wu)
@@ -134,4 +153,4 @@ def round_instance(cfg: C.Config, r: int, l: int) -> RoundResult:
     td, gd = acc.argmax_gap(zd)
     a, nxt = acc.accept(td, tv)
     return RoundResult(vo, do, zv, zd, tv, td, gv, gd, a, nxt,
-                       acc.accept_flagged(a, x, gd, gv))
+                       acc.accept_flagged(a, x, gd, gv), vs, ds)

@@ -186,3 +186,30 @@ def test_planted_mistakes_are_caught(monkeypatch):
         return real(q_, k_, v_, vis)
     monkeypatch.setattr(att, "attention", exclusive_mask)
     assert np.abs(att.verify_unit(q, kc, vc, kb, vb) - ref).max() > 1e-3
+
+
+def test_spread_closed_forms_and_unchanged_output():
+    """The weight spread sqrt(sum_t (w_t v_tc)^2): |v| of a key that takes all the weight,
+    |c| / sqrt(n) for equal weights over n keys with constant values c, a brute-force sum in
+    general; asking for it leaves the output unchanged."""
+    d, n = 8, 6
+    q = np.zeros((1, d))
+    k = RNG.normal(size=(n, d))
+    v = np.full((n, d), -3.0)
+    out, spr = att.attention(q, k, v, spread=True)           # q = 0: equal weights
+    np.testing.assert_allclose(spr, np.full((1, d), 3.0 / np.sqrt(n)), rtol=1e-14)
+    np.testing.assert_allclose(out, v[:1], rtol=1e-14)
+    q = np.zeros((1, d)); q[0, 0] = 1e4                        # one key dominates
+    k = np.zeros((n, d)); k[2, 0] = 1.0
+    v = RNG.normal(size=(n, d))
+    out, spr = att.attention(q, k, v, spread=True)
+    np.testing.assert_allclose(spr[0], np.abs(v[2]), rtol=1e-12)
+    q, k, v = RNG.normal(size=(3, d)), RNG.normal(size=(n, d)), RNG.normal(size=(n, d))
+    vis = np.tril(np.ones((3, n), dtype=bool), k=3)
+    out, spr = att.attention(q, k, v, vis, spread=True)
+    assert np.array_equal(out, att.attention(q, k, v, vis))
+    for i in range(3):
+        s = np.where(vis[i], k @ q[i] / np.sqrt(d), -np.inf)
+        w = np.exp(s - s.max()); w /= w.sum()
+        want = [math.sqrt(sum((w[t] * v[t, c]) ** 2 for t in range(n))) for c in range(d)]
+        np.testing.assert_allclose(spr[i], want, rtol=1e-12)
