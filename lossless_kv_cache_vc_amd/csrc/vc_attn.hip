@@ -1582,6 +1582,15 @@ __device__ __forceinline__ float row_max4(float x) {
   return half_swap_max(fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])));
 }
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order
+template <int N, int J = 0, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>{});
+    unroll<N, J + 1>(f);
+  }
+}
+
 template <int D, int BITS, int NW>
 __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   using R = KRing<D, BITS, NW>;
@@ -1663,8 +1672,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   asm volatile("" : "+v"(csel), "+v"(pselk), "+v"(psel0), "+v"(psel1));
   const uint32_t cstride = (uint32_t)a.Hkv * R::kCodes;
   const uint32_t kpstride = (uint32_t)a.Hkv * R::kKsz, vpstride = (uint32_t)a.Hkv * R::kVsz;
-  auto issue = [&](int k, int id0, int id1) {
-    uint8_t* slot = ring + (k % STG) * R::kSlot;
+  auto issue = [&](uint8_t* slot, int id0, int id1) {
     const uint32_t i0 = id0 < 0 ? 0u : (uint32_t)id0, i1 = id1 < 0 ? 0u : (uint32_t)id1;
     // (the differences wrap in 32 bits; every sum stays below 2^32)
     const uint32_t co = i0 * cstride + (csel & ((i1 - i0) * cstride));
@@ -1695,7 +1703,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     if (k < mine) {
       int i0, i1;
       pair_ids(k, i0, i1);
-      issue(k, __builtin_amdgcn_readfirstlane(i0), __builtin_amdgcn_readfirstlane(i1));
+      issue(ring + k * R::kSlot, __builtin_amdgcn_readfirstlane(i0), __builtin_amdgcn_readfirstlane(i1));
     }
   int pf0, pf1;  // page ids of the next slot to load, read one pair early
   pair_ids(STG - 1, pf0, pf1);
@@ -1837,12 +1845,15 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       }
     }
   };
-  auto step = [&](int k, auto full_pair) {
+  // pair k sits in slot `j` (k % STG), and the slot it refills is the one before it
+  auto step = [&](int k, int j, auto full_pair) {
     wait_ahead<R::kLoads, STG - 2>(min(STG - 2, mine - 1 - k));
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (k + STG - 1 < mine) issue(k + STG - 1, __builtin_amdgcn_readfirstlane(pf0), __builtin_amdgcn_readfirstlane(pf1));
+    if (k + STG - 1 < mine)
+      issue(ring + ((j + STG - 1) % STG) * R::kSlot, __builtin_amdgcn_readfirstlane(pf0),
+            __builtin_amdgcn_readfirstlane(pf1));
     pair_ids(k + STG, pf0, pf1);
-    const uint8_t* slot = ring + (k % STG) * R::kSlot;
+    const uint8_t* slot = ring + j * R::kSlot;
     f32x4 s_acc[2];
     scores(slot, s_acc);
     consume(k, slot, s_acc, full_pair);
@@ -1852,8 +1863,11 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   const int pairs_full = min(nfull, *first_bad) >> 1;
   const int k_full = min(mine, pairs_full > w ? (pairs_full - w + NW - 1) / NW : 0);
   int k = 0;
-  for (; k < k_full; ++k) step(k, std::true_type{});
-  for (; k < mine; ++k) step(k, std::false_type{});
+  // full pairs a ring's turn at a time: every slot offset is a constant
+  for (; k + STG <= k_full; k += STG)
+    unroll<STG>([&](auto j) { step(k + decltype(j)::value, decltype(j)::value, std::true_type{}); });
+  for (; k < k_full; ++k) step(k, k % STG, std::true_type{});
+  for (; k < mine; ++k) step(k, k % STG, std::false_type{});
 
   // the value bias joins the outputs before any pair that rescales without it
 #pragma unroll
