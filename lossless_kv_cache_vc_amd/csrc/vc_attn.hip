@@ -38,12 +38,23 @@ constexpr int kKWaves = 12;           // waves of a draft-only work-group (KIVI 
 constexpr int kKThreads = 64 * kKWaves;
 // Headroom (log2 units) a row's maximum may gain before the running maximum is moved and the
 // accumulators rescaled.  Where the weights enter the value product as bf16 (8 significant bits)
-// the running maximum moves whenever it grows: the key that sets it then has weight exactly 1,
-// which bf16 holds exactly.  With headroom, a key that dominates its row would have its weight
-// rounded by up to 2^-8 relative, an output error of up to 2^-8 |v| (over 5e-3 for rows with one
-// dominant key of a short context).  fp16 weights (11 bits) keep 8 units of headroom.
+// a key that raises the maximum must not be left with a large share of its row: the key that sets
+// the running maximum has weight exactly 1, which bf16 holds exactly, but a key above it by d
+// keeps weight 2^d, rounded by up to 2^-8 relative (an output error of up to 2^-8 |v| when it
+// dominates, over 5e-3 for short rows).  The draft paths move the maximum whenever it grows; the
+// verify paths allow the headroom rescale_headroom gives.  fp16 weights (11 bits) keep 8 units.
 constexpr float kRescaleBf16 = 0.0f;
 constexpr float kRescaleF16 = 8.0f;
+
+// Verify headroom after a move of the running maximum, from the lane's running sum l (in units of
+// the new maximum): floor(log2 l) - 3, between 0 and 8.  A key that later raises the maximum by
+// d <= headroom keeps weight 2^d <= l / 8, at most a ninth of its row (l only grows until the next
+// move, and the lane's sum is part of its row's).  Short rows, and the first tiles of long ones,
+// move the maximum on every rise; later tiles almost never.
+__device__ __forceinline__ float rescale_headroom(float l) {
+  const int e = __builtin_amdgcn_frexp_expf(l);  // l = f 2^e, f in [0.5, 1): floor(log2 l) = e - 1
+  return fminf(8.f, fmaxf(0.f, (float)(e - 4)));
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ bf16x8 as_bf(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -353,6 +364,7 @@ struct VerifyState {
   u32x4 qreg[NS];         // query rows: B operand of S^T = K Q^T
   f32x16 acc_o[ND];
   float m_run, l_run, sc;
+  float thr;              // headroom before the running maximum moves (rescale_headroom)
 };
 
 // Global address of page `ip` of the item (scalar): a context page (its unit, or the dummy when
@@ -445,9 +457,10 @@ __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>
   mloc = half_swap_max(mloc);
   const float sc = vs.sc;
   const float m_new = fmaxf(vs.m_run, mloc * sc);
-  if (__any(m_new > vs.m_run + kRescaleBf16)) {
+  if (__any(m_new > vs.m_run + vs.thr)) {
     const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
     vs.l_run *= alpha;
+    vs.thr = rescale_headroom(vs.l_run);
 #pragma unroll
     for (int i = 0; i < ND; ++i) vs.acc_o[i] *= alpha;
     vs.m_run = m_new;
@@ -501,9 +514,10 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
   mloc = half_swap_max(mloc);
   const float sc = vs.sc;
   const float m_new = fmaxf(vs.m_run, mloc * sc);
-  if (__any(m_new > vs.m_run + kRescaleBf16)) {
+  if (__any(m_new > vs.m_run + vs.thr)) {
     const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
     vs.l_run *= alpha;
+    vs.thr = rescale_headroom(vs.l_run);
 #pragma unroll
     for (int i = 0; i < ND; ++i) vs.acc_o[i] *= alpha;
     vs.m_run = m_new;
@@ -651,6 +665,7 @@ __device__ __forceinline__ void verify_begin(const AttnArgs& a, const ItemCtx& i
   for (int i = 0; i < VerifyState<D>::ND; ++i) vs.acc_o[i] = f32x16{};
   vs.m_run = -INFINITY;
   vs.l_run = 0.f;
+  vs.thr = 0.f;
 }
 
 template <int D>
