@@ -365,6 +365,8 @@ struct VerifyState {
   f32x16 acc_o[ND];
   float m_run, l_run, sc;
   float thr;              // headroom before the running maximum moves (rescale_headroom)
+  const uint8_t* kv_pool;  // the pool this wave loads from (K for key waves, V for value waves)
+  const uint16_t* kv_blk;  // and its drafted-block array
 };
 
 // Global address of page `ip` of the item (scalar): a context page (its unit, or the dummy when
@@ -385,28 +387,23 @@ __device__ __forceinline__ const uint8_t* verify_page(const uint8_t* pool_base, 
 // Issue this wave's page of tile t into ring stage `stage`.  Every wave issues the same number
 // of loads per tile (a missing page reads the dummy and is masked when consumed), so vmcnt
 // counts are exact.
-template <int D>
-__device__ __forceinline__ void verify_issue(const AttnArgs& a, const ItemCtx& it, const VerifyState<D>& vs,
-                                             uint8_t* smem, int t, int stage, int unit) {
+// SHARED: the loads keep their lines in L2 for other row groups of the unit (else they stream).
+// CTX: tile t is one of the item's leading full, valid context tiles (t < t_full), whose pages
+// are the units themselves.
+template <int D, bool SHARED, bool CTX = false>
+__device__ __forceinline__ void verify_issue(const ItemCtx& it, const VerifyState<D>& vs, uint8_t* smem,
+                                             int t, int stage, int unit) {
   using R = VRing<D>;
-  const int ip = 4 * t + vs.ps;
-  // K and V are separate calls: choosing between descriptor fields by reference would make
-  // the compiler copy the kernel argument block to scratch
-  const uint8_t* page = vs.kwave ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip, unit)
-                                 : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip, unit);
+  const uint8_t* page;
+  if constexpr (CTX)
+    page = vs.kv_pool + (int64_t)__builtin_amdgcn_readfirstlane(unit) * R::kPage;
+  else
+    page = verify_page<D>(vs.kv_pool, vs.kv_blk, it, vs, 4 * t + vs.ps, unit);
   uint8_t* dst = smem + (vs.kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;  // stage < 4 (K) or < 5 (V)
-  if (vs.shared_kv) {  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < R::kLoads; ++i) {
-      const void* src = page + vs.lane_off[i];
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, kTemporal);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < R::kLoads; ++i) {
-      const void* src = page + vs.lane_off[i];
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, kNontemporal);
-    }
+  for (int i = 0; i < R::kLoads; ++i) {
+    const void* src = page + vs.lane_off[i];
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + i * 1024), 16, 0, SHARED ? kTemporal : kNontemporal);
   }
 }
 
@@ -569,9 +566,9 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
 // into key stage t % 4, V(t + 3) into value stage (t - 1) % 4), score tile t + 1 into s_nxt (the
 // last tile scores a stale stage, unused) and consume tile t.  STC >= 0: t % 4 == STC known at
 // compile time.
-template <int D, int STC, bool MASK, bool STEADY = false>
-__device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs,
-                                            uint8_t* smem, int t, f32x16& s_cur, f32x16& s_nxt) {
+template <int D, bool SHARED, int STC, bool MASK, bool STEADY = false, bool CTX = false>
+__device__ __forceinline__ void verify_step(const ItemCtx& it, VerifyState<D>& vs, uint8_t* smem, int t,
+                                            f32x16& s_cur, f32x16& s_nxt) {
   const int st = STC >= 0 ? STC : (t & (kVStages - 1));
   const int ntiles = vs.ntiles;
   // keys: K(t + 1) must have landed (K issued up to t + 3); values: V(t) (V issued up to t + 3).
@@ -590,7 +587,7 @@ __device__ __forceinline__ void verify_step(const AttnArgs& a, const ItemCtx& it
   // then read the unit for the next tile's load
   const int vst = vs.vst;
   const int vst4 = vst == 0 ? kVVStages - 1 : vst - 1;  // (t + 4) % 5
-  if (STEADY || t + 4 < ntiles) verify_issue<D>(a, it, vs, smem, t + 4, vs.kwave ? st : vst4, vs.pf_unit);
+  if (STEADY || t + 4 < ntiles) verify_issue<D, SHARED, CTX>(it, vs, smem, t + 4, vs.kwave ? st : vst4, vs.pf_unit);
   {
     const int ipn = 4 * (t + 5) + vs.ps;
     vs.pf_unit = ipn < it.nctx ? vs.units[ipn] : -1;
@@ -668,8 +665,62 @@ __device__ __forceinline__ void verify_begin(const AttnArgs& a, const ItemCtx& i
   vs.thr = 0.f;
 }
 
+// The ring loop of a verify item: prologue, then full tiles (no masking) four at a time, so ring
+// stages are compile-time and the scores alternate between s_a and s_b without register copies;
+// then the rest, with masking.  The accumulators are left in vs.
+template <int D, bool SHARED>
+__device__ __forceinline__ void verify_tiles(const ItemCtx& it, VerifyState<D>& vs, uint8_t* smem,
+                                          const int32_t* units) {
+  const int ntiles = vs.ntiles;
+  // prologue: K(0..3) and V(0..3) into stages 0..3; scores of tile 0
+  const int kpro = min(ntiles, 4);
+  for (int j = 0; j < kpro; ++j) {
+    const int ip = 4 * j + vs.ps;
+    verify_issue<D, SHARED>(it, vs, smem, j, j, ip < it.nctx ? units[ip] : -1);
+  }
+  {
+    const int ipn = 4 * 4 + vs.ps;
+    vs.pf_unit = ipn < it.nctx ? units[ipn] : -1;
+  }
+  vs.vst = 0;
+  if (vs.kwave) wait_tiles<D>(kpro - 1);  // K(0)
+  ring_barrier();
+  f32x16 s_a = vs.wave_on ? verify_scores<D>(smem, 0, vs) : f32x16{};
+  f32x16 s_b = f32x16{};
+
+  int t = 0;
+  // steady state: every step of the group issues its refill (t + 7 < ntiles); while the
+  // refills are full context tiles too (t + 7 < t_full) their pages are the units themselves
+  for (; t + 7 < vs.t_full; t += 4) {
+    verify_step<D, SHARED, 0, false, true, true>(it, vs, smem, t, s_a, s_b);
+    verify_step<D, SHARED, 1, false, true, true>(it, vs, smem, t + 1, s_b, s_a);
+    verify_step<D, SHARED, 2, false, true, true>(it, vs, smem, t + 2, s_a, s_b);
+    verify_step<D, SHARED, 3, false, true, true>(it, vs, smem, t + 3, s_b, s_a);
+  }
+  for (; t + 3 < vs.t_full && t + 7 < ntiles; t += 4) {
+    verify_step<D, SHARED, 0, false, true>(it, vs, smem, t, s_a, s_b);
+    verify_step<D, SHARED, 1, false, true>(it, vs, smem, t + 1, s_b, s_a);
+    verify_step<D, SHARED, 2, false, true>(it, vs, smem, t + 2, s_a, s_b);
+    verify_step<D, SHARED, 3, false, true>(it, vs, smem, t + 3, s_b, s_a);
+  }
+  for (; t + 3 < vs.t_full; t += 4) {
+    verify_step<D, SHARED, 0, false>(it, vs, smem, t, s_a, s_b);
+    verify_step<D, SHARED, 1, false>(it, vs, smem, t + 1, s_b, s_a);
+    verify_step<D, SHARED, 2, false>(it, vs, smem, t + 2, s_a, s_b);
+    verify_step<D, SHARED, 3, false>(it, vs, smem, t + 3, s_b, s_a);
+  }
+  for (; t < vs.t_full; ++t) {
+    verify_step<D, SHARED, -1, false>(it, vs, smem, t, s_a, s_b);
+    s_a = s_b;
+  }
+  for (; t < ntiles; ++t) {
+    verify_step<D, SHARED, -1, true>(it, vs, smem, t, s_a, s_b);
+    s_a = s_b;
+  }
+}
+
 template <int D>
-__device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
+__device__ __forceinline__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_t* smem) {
   using R = VRing<D>;
   using VS = VerifyState<D>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -701,46 +752,12 @@ __device__ void verify_item(const AttnArgs& a, const ItemCtx& it, int rg, uint8_
     vs.voff = R::kV0 + 2 * vs.kh * R::kPage + n * 32 + ((h ^ ((n >> 3) & 1)) * 16);
   }
 
-  // prologue: K(0..3) and V(0..3) into stages 0..3; scores of tile 0
-  const int kpro = min(ntiles, 4);
-  for (int j = 0; j < kpro; ++j) {
-    const int ip = 4 * j + vs.ps;
-    verify_issue<D>(a, it, vs, smem, j, j, ip < it.nctx ? units[ip] : -1);
-  }
-  {
-    const int ipn = 4 * 4 + vs.ps;
-    vs.pf_unit = ipn < it.nctx ? units[ipn] : -1;
-  }
-  vs.vst = 0;
-  if (vs.kwave) wait_tiles<D>(kpro - 1);  // K(0)
-  ring_barrier();
-  f32x16 s_a = vs.wave_on ? verify_scores<D>(smem, 0, vs) : f32x16{};
-  f32x16 s_b = f32x16{};
-
-  // full tiles (no masking) four at a time, so ring stages are compile-time and the scores
-  // alternate between s_a and s_b without register copies; then the rest, with masking
-  int t = 0;
-  // steady state: every step of the group issues its refill (t + 7 < ntiles)
-  for (; t + 3 < vs.t_full && t + 7 < ntiles; t += 4) {
-    verify_step<D, 0, false, true>(a, it, vs, smem, t, s_a, s_b);
-    verify_step<D, 1, false, true>(a, it, vs, smem, t + 1, s_b, s_a);
-    verify_step<D, 2, false, true>(a, it, vs, smem, t + 2, s_a, s_b);
-    verify_step<D, 3, false, true>(a, it, vs, smem, t + 3, s_b, s_a);
-  }
-  for (; t + 3 < vs.t_full; t += 4) {
-    verify_step<D, 0, false>(a, it, vs, smem, t, s_a, s_b);
-    verify_step<D, 1, false>(a, it, vs, smem, t + 1, s_b, s_a);
-    verify_step<D, 2, false>(a, it, vs, smem, t + 2, s_a, s_b);
-    verify_step<D, 3, false>(a, it, vs, smem, t + 3, s_b, s_a);
-  }
-  for (; t < vs.t_full; ++t) {
-    verify_step<D, -1, false>(a, it, vs, smem, t, s_a, s_b);
-    s_a = s_b;
-  }
-  for (; t < ntiles; ++t) {
-    verify_step<D, -1, true>(a, it, vs, smem, t, s_a, s_b);
-    s_a = s_b;
-  }
+  // K and V are chosen by value here, once: choosing between descriptor fields by reference
+  // would make the compiler copy the kernel argument block to scratch
+  vs.kv_pool = vs.kwave ? it.pool.k : it.pool.v;
+  vs.kv_blk = vs.kwave ? a.blk_k : a.blk_v;
+  if (vs.shared_kv) verify_tiles<D, true>(it, vs, smem, units);  // wave-uniform
+  else verify_tiles<D, false>(it, vs, smem, units);
 
   // merge the two key halves of every row block through LDS (the ring is free now)
   __syncthreads();
