@@ -835,6 +835,11 @@ struct WideLoads {
   int s0, s1;
   int pf0, pf1;         // units of the pages the slots load next (read from LDS a tile early)
   uint32_t off0, off1;  // lane offsets of each slot's load 0 (see ring_load_step)
+  // each slot's pool and drafted-block array (K for slots 0-3, V for 4-7), chosen once by value
+  const uint8_t* pool0;
+  const uint8_t* pool1;
+  const uint16_t* blk0;
+  const uint16_t* blk1;
 };
 
 // Unit of context page ip of the item, -1 past the context (drafted block or nothing).
@@ -843,15 +848,19 @@ __device__ __forceinline__ int unit_at(const int32_t* units, const ItemCtx& it, 
 }
 
 // Issue ring slot `slot` of tile t into stage `stage`.
-template <int D>
-__device__ __forceinline__ void wide_issue(const AttnArgs& a, const ItemCtx& it, const VerifyState<D>& vs,
-                                           uint8_t* smem, int slot, uint32_t off, int t, int stage, int unit) {
+// CTX: tile t is one of the item's leading full, valid context tiles (its pages are the units).
+template <int D, bool CTX = false>
+__device__ __forceinline__ void wide_issue(const ItemCtx& it, const VerifyState<D>& vs, uint8_t* smem, int slot,
+                                           const uint8_t* pool, const uint16_t* blk, uint32_t off, int t,
+                                           int stage, int unit) {
   using R = WRing<D>;
   const int ps = slot & 3;
-  const int ip = 4 * t + ps;
   const bool key = slot < 4;
-  const uint8_t* page = key ? verify_page<D>(it.pool.k, a.blk_k, it, vs, ip, unit)
-                            : verify_page<D>(it.pool.v, a.blk_v, it, vs, ip, unit);
+  const uint8_t* page;
+  if constexpr (CTX)
+    page = pool + (int64_t)__builtin_amdgcn_readfirstlane(unit) * R::kPage;
+  else
+    page = verify_page<D>(pool, blk, it, vs, 4 * t + ps, unit);
   uint8_t* dst = smem + (key ? 0 : R::kV0) + stage * R::kTile + ps * R::kPage;
   const uint32_t step = ring_load_step(key);
   asm volatile("" : "+v"(off));  // derive the load offsets here, not as registers held in the loop
@@ -893,18 +902,17 @@ __device__ __forceinline__ f32x16 wide_scores(const uint8_t* smem, int st, uint3
 
 // One tile: wait for tile t, refill the stage freed by tile t - 1 with tile t + 3, then both
 // key halves of tile t, one after the other.  STC >= 0: t % 4 == STC known at compile time.
-template <int D, int STC, bool MASK, bool SPLIT>
-__device__ __forceinline__ void wide_step(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs,
-                                          WideLoads& ld, uint8_t* smem, int t, uint32_t kx, uint32_t voff0,
-                                          int kh_only) {
+template <int D, int STC, bool MASK, bool SPLIT, bool CTX = false>
+__device__ __forceinline__ void wide_step(const ItemCtx& it, VerifyState<D>& vs, WideLoads& ld, uint8_t* smem,
+                                          int t, uint32_t kx, uint32_t voff0, int kh_only) {
   const int st = STC >= 0 ? STC : (t & (kWStages - 1));
   const int ntiles = vs.ntiles;
   wide_wait<D>(ld.nslot, min(2, ntiles - 1 - t));
   ring_barrier();
   if (t + 3 < ntiles) {
     const int sn = (st + 3) & (kWStages - 1);
-    if (ld.nslot >= 1) wide_issue<D>(a, it, vs, smem, ld.s0, ld.off0, t + 3, sn, ld.pf0);
-    if (ld.nslot == 2) wide_issue<D>(a, it, vs, smem, ld.s1, ld.off1, t + 3, sn, ld.pf1);
+    if (ld.nslot >= 1) wide_issue<D, CTX>(it, vs, smem, ld.s0, ld.pool0, ld.blk0, ld.off0, t + 3, sn, ld.pf0);
+    if (ld.nslot == 2) wide_issue<D, CTX>(it, vs, smem, ld.s1, ld.pool1, ld.blk1, ld.off1, t + 3, sn, ld.pf1);
   }
   ld.pf0 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s0 & 3));
   ld.pf1 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s1 & 3));
@@ -927,18 +935,26 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const ItemCtx& it, 
 // The tile loop of a wide verify wave: full tiles four at a time with compile-time ring stages,
 // then the rest, then the masked tiles.  SPLIT: the wave takes one key half of every tile.
 template <int D, bool SPLIT>
-__device__ __forceinline__ void wide_loop(const AttnArgs& a, const ItemCtx& it, VerifyState<D>& vs, WideLoads& ld,
-                                          uint8_t* smem, uint32_t kx, uint32_t voff0, int kh_only) {
+__device__ __forceinline__ void wide_loop(const ItemCtx& it, VerifyState<D>& vs, WideLoads& ld, uint8_t* smem,
+                                          uint32_t kx, uint32_t voff0, int kh_only) {
   const int ntiles = vs.ntiles;
   int t = 0;
-  for (; t + 3 < vs.t_full; t += 4) {
-    wide_step<D, 0, false, SPLIT>(a, it, vs, ld, smem, t, kx, voff0, kh_only);
-    wide_step<D, 1, false, SPLIT>(a, it, vs, ld, smem, t + 1, kx, voff0, kh_only);
-    wide_step<D, 2, false, SPLIT>(a, it, vs, ld, smem, t + 2, kx, voff0, kh_only);
-    wide_step<D, 3, false, SPLIT>(a, it, vs, ld, smem, t + 3, kx, voff0, kh_only);
+  // while the refills (tiles t + 3 .. t + 6) are leading full context tiles too, their pages
+  // are the units themselves
+  for (; t + 6 < vs.t_full; t += 4) {
+    wide_step<D, 0, false, SPLIT, true>(it, vs, ld, smem, t, kx, voff0, kh_only);
+    wide_step<D, 1, false, SPLIT, true>(it, vs, ld, smem, t + 1, kx, voff0, kh_only);
+    wide_step<D, 2, false, SPLIT, true>(it, vs, ld, smem, t + 2, kx, voff0, kh_only);
+    wide_step<D, 3, false, SPLIT, true>(it, vs, ld, smem, t + 3, kx, voff0, kh_only);
   }
-  for (; t < vs.t_full; ++t) wide_step<D, -1, false, SPLIT>(a, it, vs, ld, smem, t, kx, voff0, kh_only);
-  for (; t < ntiles; ++t) wide_step<D, -1, true, SPLIT>(a, it, vs, ld, smem, t, kx, voff0, kh_only);
+  for (; t + 3 < vs.t_full; t += 4) {
+    wide_step<D, 0, false, SPLIT>(it, vs, ld, smem, t, kx, voff0, kh_only);
+    wide_step<D, 1, false, SPLIT>(it, vs, ld, smem, t + 1, kx, voff0, kh_only);
+    wide_step<D, 2, false, SPLIT>(it, vs, ld, smem, t + 2, kx, voff0, kh_only);
+    wide_step<D, 3, false, SPLIT>(it, vs, ld, smem, t + 3, kx, voff0, kh_only);
+  }
+  for (; t < vs.t_full; ++t) wide_step<D, -1, false, SPLIT>(it, vs, ld, smem, t, kx, voff0, kh_only);
+  for (; t < ntiles; ++t) wide_step<D, -1, true, SPLIT>(it, vs, ld, smem, t, kx, voff0, kh_only);
 }
 
 template <int D>
@@ -974,6 +990,10 @@ __device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, u
   ld.nslot = (ld.s0 < 8) + (ld.s1 < 8);
   ld.off0 = ring_lane_off<D>(ld.s0 < 4, lane, 0);
   ld.off1 = ring_lane_off<D>(ld.s1 < 4, lane, 0);
+  ld.pool0 = ld.s0 < 4 ? it.pool.k : it.pool.v;
+  ld.pool1 = ld.s1 < 4 ? it.pool.k : it.pool.v;
+  ld.blk0 = ld.s0 < 4 ? a.blk_k : a.blk_v;
+  ld.blk1 = ld.s1 < 4 ? a.blk_k : a.blk_v;
   const int key = key_of_m32(n);
   const uint32_t kx = key * (2 * D) | ((h ^ swz_k<D>(key)) << 4);
   const uint32_t voff0 = R::kV0 + n * 32 + ((h ^ ((n >> 3) & 1)) * 16);
@@ -981,14 +1001,16 @@ __device__ void verify_wide_item(const AttnArgs& a, const ItemCtx& it, int rg, u
   // prologue: tiles 0..2 into stages 0..2
   const int kpro = min(ntiles, 3);
   for (int j = 0; j < kpro; ++j) {
-    if (ld.nslot >= 1) wide_issue<D>(a, it, vs, smem, ld.s0, ld.off0, j, j, unit_at(units, it, 4 * j + (ld.s0 & 3)));
-    if (ld.nslot == 2) wide_issue<D>(a, it, vs, smem, ld.s1, ld.off1, j, j, unit_at(units, it, 4 * j + (ld.s1 & 3)));
+    if (ld.nslot >= 1)
+      wide_issue<D>(it, vs, smem, ld.s0, ld.pool0, ld.blk0, ld.off0, j, j, unit_at(units, it, 4 * j + (ld.s0 & 3)));
+    if (ld.nslot == 2)
+      wide_issue<D>(it, vs, smem, ld.s1, ld.pool1, ld.blk1, ld.off1, j, j, unit_at(units, it, 4 * j + (ld.s1 & 3)));
   }
   ld.pf0 = unit_at(units, it, 12 + (ld.s0 & 3));
   ld.pf1 = unit_at(units, it, 12 + (ld.s1 & 3));
 
-  if (split) wide_loop<D, true>(a, it, vs, ld, smem, kx, voff0, kh_only);
-  else wide_loop<D, false>(a, it, vs, ld, smem, kx, voff0, kh_only);
+  if (split) wide_loop<D, true>(it, vs, ld, smem, kx, voff0, kh_only);
+  else wide_loop<D, false>(it, vs, ld, smem, kx, voff0, kh_only);
 
   // the two halves of a shared row block merge through LDS (the ring is free now): the key-half-1
   // wave leaves its state, the key-half-0 wave combines and writes
