@@ -390,7 +390,8 @@ __device__ __forceinline__ const uint8_t* verify_page(const uint8_t* pool_base, 
 // SHARED: the loads keep their lines in L2 for other row groups of the unit (else they stream).
 // CTX: tile t is one of the item's leading full, valid context tiles (t < t_full), whose pages
 // are the units themselves.
-template <int D, bool SHARED, bool CTX = false>
+// KW: the wave loads keys (1) or values (0), known at compile time, or -1 (read from vs.kwave).
+template <int D, bool SHARED, bool CTX = false, int KW = -1>
 __device__ __forceinline__ void verify_issue(const ItemCtx& it, const VerifyState<D>& vs, uint8_t* smem,
                                              int t, int stage, int unit) {
   using R = VRing<D>;
@@ -399,7 +400,8 @@ __device__ __forceinline__ void verify_issue(const ItemCtx& it, const VerifyStat
     page = vs.kv_pool + (int64_t)__builtin_amdgcn_readfirstlane(unit) * R::kPage;
   else
     page = verify_page<D>(vs.kv_pool, vs.kv_blk, it, vs, 4 * t + vs.ps, unit);
-  uint8_t* dst = smem + (vs.kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;  // stage < 4 (K) or < 5 (V)
+  const bool kwave = KW >= 0 ? KW == 1 : vs.kwave;
+  uint8_t* dst = smem + (kwave ? 0 : R::kV0) + stage * R::kTileK + vs.ps * R::kPage;  // stage < 4 (K) or < 5 (V)
 #pragma unroll
   for (int i = 0; i < R::kLoads; ++i) {
     const void* src = page + vs.lane_off[i];
@@ -566,17 +568,18 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
 // into key stage t % 4, V(t + 3) into value stage (t - 1) % 4), score tile t + 1 into s_nxt (the
 // last tile scores a stale stage, unused) and consume tile t.  STC >= 0: t % 4 == STC known at
 // compile time.
-template <int D, bool SHARED, int STC, bool MASK, bool STEADY = false, bool CTX = false>
+template <int D, bool SHARED, int STC, bool MASK, bool STEADY = false, bool CTX = false, int KW = -1>
 __device__ __forceinline__ void verify_step(const ItemCtx& it, VerifyState<D>& vs, uint8_t* smem, int t,
                                             f32x16& s_cur, f32x16& s_nxt) {
   const int st = STC >= 0 ? STC : (t & (kVStages - 1));
   const int ntiles = vs.ntiles;
+  const bool kwave = KW >= 0 ? KW == 1 : vs.kwave;
   // keys: K(t + 1) must have landed (K issued up to t + 3); values: V(t) (V issued up to t + 3).
   // STEADY: t + 4 < ntiles, so both waits leave three tiles in flight and the refill is issued.
   if constexpr (STEADY) {
-    if (vs.kwave) wait_tiles<D>(2);
+    if (kwave) wait_tiles<D>(2);
     else wait_tiles<D>(3);
-  } else if (vs.kwave) {
+  } else if (kwave) {
     if (t + 1 < ntiles) wait_tiles<D>(min(2, ntiles - t - 2));
   } else {
     wait_tiles<D>(min(3, ntiles - t - 1));
@@ -587,10 +590,11 @@ __device__ __forceinline__ void verify_step(const ItemCtx& it, VerifyState<D>& v
   // then read the unit for the next tile's load
   const int vst = vs.vst;
   const int vst4 = vst == 0 ? kVVStages - 1 : vst - 1;  // (t + 4) % 5
-  if (STEADY || t + 4 < ntiles) verify_issue<D, SHARED, CTX>(it, vs, smem, t + 4, vs.kwave ? st : vst4, vs.pf_unit);
+  if (STEADY || t + 4 < ntiles) verify_issue<D, SHARED, CTX, KW>(it, vs, smem, t + 4, kwave ? st : vst4, vs.pf_unit);
   {
+    // (CTX: tile t + 5 is a full context tile too)
     const int ipn = 4 * (t + 5) + vs.ps;
-    vs.pf_unit = ipn < it.nctx ? vs.units[ipn] : -1;
+    vs.pf_unit = (CTX || ipn < it.nctx) ? vs.units[ipn] : -1;
   }
   vs.vst = vst == kVVStages - 1 ? 0 : vst + 1;
   if (!vs.wave_on) return;
@@ -665,6 +669,21 @@ __device__ __forceinline__ void verify_begin(const AttnArgs& a, const ItemCtx& i
   vs.thr = 0.f;
 }
 
+// Steady tiles of a verify item whose refills are leading full context tiles, four at a time,
+// for a key (KW = 1) or value (KW = 0) wave; returns the first tile not taken.
+template <int D, bool SHARED, int KW>
+__device__ __forceinline__ int verify_ctx_tiles(const ItemCtx& it, VerifyState<D>& vs, uint8_t* smem, f32x16& s_a,
+                                                f32x16& s_b) {
+  int t = 0;
+  for (; t + 7 < vs.t_full; t += 4) {
+    verify_step<D, SHARED, 0, false, true, true, KW>(it, vs, smem, t, s_a, s_b);
+    verify_step<D, SHARED, 1, false, true, true, KW>(it, vs, smem, t + 1, s_b, s_a);
+    verify_step<D, SHARED, 2, false, true, true, KW>(it, vs, smem, t + 2, s_a, s_b);
+    verify_step<D, SHARED, 3, false, true, true, KW>(it, vs, smem, t + 3, s_b, s_a);
+  }
+  return t;
+}
+
 // The ring loop of a verify item: prologue, then full tiles (no masking) four at a time, so ring
 // stages are compile-time and the scores alternate between s_a and s_b without register copies;
 // then the rest, with masking.  The accumulators are left in vs.
@@ -690,13 +709,10 @@ __device__ __forceinline__ void verify_tiles(const ItemCtx& it, VerifyState<D>& 
 
   int t = 0;
   // steady state: every step of the group issues its refill (t + 7 < ntiles); while the
-  // refills are full context tiles too (t + 7 < t_full) their pages are the units themselves
-  for (; t + 7 < vs.t_full; t += 4) {
-    verify_step<D, SHARED, 0, false, true, true>(it, vs, smem, t, s_a, s_b);
-    verify_step<D, SHARED, 1, false, true, true>(it, vs, smem, t + 1, s_b, s_a);
-    verify_step<D, SHARED, 2, false, true, true>(it, vs, smem, t + 2, s_a, s_b);
-    verify_step<D, SHARED, 3, false, true, true>(it, vs, smem, t + 3, s_b, s_a);
-  }
+  // refills are full context tiles too (t + 7 < t_full) their pages are the units themselves,
+  // and the wave's role (keys or values) is a compile-time constant
+  if (vs.kwave) t = verify_ctx_tiles<D, SHARED, 1>(it, vs, smem, s_a, s_b);
+  else t = verify_ctx_tiles<D, SHARED, 0>(it, vs, smem, s_a, s_b);
   for (; t + 3 < vs.t_full && t + 7 < ntiles; t += 4) {
     verify_step<D, SHARED, 0, false, true>(it, vs, smem, t, s_a, s_b);
     verify_step<D, SHARED, 1, false, true>(it, vs, smem, t + 1, s_b, s_a);
