@@ -923,15 +923,22 @@ __device__ __forceinline__ void wide_step(const ItemCtx& it, VerifyState<D>& vs,
                                           int t, uint32_t kx, uint32_t voff0, int kh_only) {
   const int st = STC >= 0 ? STC : (t & (kWStages - 1));
   const int ntiles = vs.ntiles;
-  wide_wait<D>(ld.nslot, min(2, ntiles - 1 - t));
+  // (CTX: tiles t + 3 and t + 4 are full context tiles, so two tiles are always ahead and the
+  // next units are in the table)
+  wide_wait<D>(ld.nslot, CTX ? 2 : min(2, ntiles - 1 - t));
   ring_barrier();
-  if (t + 3 < ntiles) {
+  if (CTX || t + 3 < ntiles) {
     const int sn = (st + 3) & (kWStages - 1);
     if (ld.nslot >= 1) wide_issue<D, CTX>(it, vs, smem, ld.s0, ld.pool0, ld.blk0, ld.off0, t + 3, sn, ld.pf0);
     if (ld.nslot == 2) wide_issue<D, CTX>(it, vs, smem, ld.s1, ld.pool1, ld.blk1, ld.off1, t + 3, sn, ld.pf1);
   }
-  ld.pf0 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s0 & 3));
-  ld.pf1 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s1 & 3));
+  if constexpr (CTX) {
+    ld.pf0 = vs.units[4 * (t + 4) + (ld.s0 & 3)];
+    ld.pf1 = vs.units[4 * (t + 4) + (ld.s1 & 3)];
+  } else {
+    ld.pf0 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s0 & 3));
+    ld.pf1 = unit_at(vs.units, it, 4 * (t + 4) + (ld.s1 & 3));
+  }
   if (!vs.wave_on) return;
   asm volatile("" : "+v"(kx));  // the 8 operand offsets kx ^ 32 s are derived here, not held
   if constexpr (SPLIT) {  // one key half (kh_only) of a shared row block
