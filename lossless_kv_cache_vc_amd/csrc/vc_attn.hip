@@ -592,9 +592,9 @@ __device__ __forceinline__ void verify_step(const ItemCtx& it, VerifyState<D>& v
   const int vst4 = vst == 0 ? kVVStages - 1 : vst - 1;  // (t + 4) % 5
   if (STEADY || t + 4 < ntiles) verify_issue<D, SHARED, CTX, KW>(it, vs, smem, t + 4, kwave ? st : vst4, vs.pf_unit);
   {
-    // (CTX: tile t + 5 is a full context tile too)
+    // (CTX: tile t + 5 is a full context tile too, except at the last step of a group of four)
     const int ipn = 4 * (t + 5) + vs.ps;
-    vs.pf_unit = (CTX || ipn < it.nctx) ? vs.units[ipn] : -1;
+    vs.pf_unit = ((CTX && STC >= 0 && STC < 3) || ipn < it.nctx) ? vs.units[ipn] : -1;
   }
   vs.vst = vst == kVVStages - 1 ? 0 : vst + 1;
   if (!vs.wave_on) return;
@@ -923,8 +923,8 @@ __device__ __forceinline__ void wide_step(const ItemCtx& it, VerifyState<D>& vs,
                                           int t, uint32_t kx, uint32_t voff0, int kh_only) {
   const int st = STC >= 0 ? STC : (t & (kWStages - 1));
   const int ntiles = vs.ntiles;
-  // (CTX: tiles t + 3 and t + 4 are full context tiles, so two tiles are always ahead and the
-  // next units are in the table)
+  // (CTX: tile t + 3 is a full context tile, so two tiles are always ahead; so is tile t + 4,
+  // whose units are read next, except at the last step of a group of four)
   wide_wait<D>(ld.nslot, CTX ? 2 : min(2, ntiles - 1 - t));
   ring_barrier();
   if (CTX || t + 3 < ntiles) {
@@ -932,7 +932,7 @@ __device__ __forceinline__ void wide_step(const ItemCtx& it, VerifyState<D>& vs,
     if (ld.nslot >= 1) wide_issue<D, CTX>(it, vs, smem, ld.s0, ld.pool0, ld.blk0, ld.off0, t + 3, sn, ld.pf0);
     if (ld.nslot == 2) wide_issue<D, CTX>(it, vs, smem, ld.s1, ld.pool1, ld.blk1, ld.off1, t + 3, sn, ld.pf1);
   }
-  if constexpr (CTX) {
+  if constexpr (CTX && STC >= 0 && STC < 3) {
     ld.pf0 = vs.units[4 * (t + 4) + (ld.s0 & 3)];
     ld.pf1 = vs.units[4 * (t + 4) + (ld.s1 & 3)];
   } else {
