@@ -179,6 +179,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
   const int chunk = split_pages > 0 ? split_pages : auto_chunk(s, nreq, reqs, vwaves);
   plan->any_split = 0;
   plan->has_verify = plan->has_draft = 0;
+  plan->draft_bits = 0;
   table->assign(nreq, ReqDev{});
   std::vector<double> item_cost(nreq, 0.0);
   for (int i = 0; i < nreq; ++i) {
@@ -218,6 +219,7 @@ int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const
       return fail(VC_EINVAL, buf);
     }
     (r.kind == VC_VERIFY ? plan->has_verify : plan->has_draft) = 1;
+    if (r.kind == VC_DRAFT) plan->draft_bits = (plan->draft_bits == 0 || plan->draft_bits == p.bits) ? p.bits : -1;
     ReqDev& d = (*table)[i];
     d.slot = r.slot;
     d.pool = r.pool;

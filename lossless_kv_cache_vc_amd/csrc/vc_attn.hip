@@ -2191,18 +2191,23 @@ int launch_attn(const AttnArgs& args, const Plan& plan, int head_dim, hipStream_
     const dim3 block(64 * wide_waves(args.vwaves, &nfull));
     if (head_dim == 128) hipLaunchKernelGGL(verify_wide_kernel<128>, grid, block, 0, stream, args);
     else hipLaunchKernelGGL(verify_wide_kernel<64>, grid, block, 0, stream, args);
-  } else if (head_dim == 128) {
-    if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
-    else if (has_v) hipLaunchKernelGGL(verify_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
-    else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<128>, grid, dim3(kDThreads), 0, stream, args);
-    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<128, 2>), grid, dim3(kKThreads), 0, stream, args);
-    else hipLaunchKernelGGL((draft_kivi_kernel<128, 4>), grid, dim3(kKThreads), 0, stream, args);
   } else {
-    if (has_v && has_d) hipLaunchKernelGGL(mixed_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
-    else if (has_v) hipLaunchKernelGGL(verify_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
-    else if (args.pools[0].bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<64>, grid, dim3(kDThreads), 0, stream, args);
-    else if (args.pools[0].bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<64, 2>), grid, dim3(kKThreads), 0, stream, args);
-    else hipLaunchKernelGGL((draft_kivi_kernel<64, 4>), grid, dim3(kKThreads), 0, stream, args);
+    // a draft-only launch runs the draft kernel of its pools' kind; drafting requests over pools
+    // of several kinds (any pool index) take the mixed kernel, which picks the path per item
+    const bool mixed = (has_v && has_d) || (has_d && plan.draft_bits < 0);
+    if (head_dim == 128) {
+      if (mixed) hipLaunchKernelGGL(mixed_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
+      else if (has_v) hipLaunchKernelGGL(verify_kernel<128>, grid, dim3(kVThreads), 0, stream, args);
+      else if (plan.draft_bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<128>, grid, dim3(kDThreads), 0, stream, args);
+      else if (plan.draft_bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<128, 2>), grid, dim3(kKThreads), 0, stream, args);
+      else hipLaunchKernelGGL((draft_kivi_kernel<128, 4>), grid, dim3(kKThreads), 0, stream, args);
+    } else {
+      if (mixed) hipLaunchKernelGGL(mixed_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
+      else if (has_v) hipLaunchKernelGGL(verify_kernel<64>, grid, dim3(kVThreads), 0, stream, args);
+      else if (plan.draft_bits == 16) hipLaunchKernelGGL(draft_bf16_kernel<64>, grid, dim3(kDThreads), 0, stream, args);
+      else if (plan.draft_bits == 2) hipLaunchKernelGGL((draft_kivi_kernel<64, 2>), grid, dim3(kKThreads), 0, stream, args);
+      else hipLaunchKernelGGL((draft_kivi_kernel<64, 4>), grid, dim3(kKThreads), 0, stream, args);
+    }
   }
   int rc = hip_check(hipGetLastError(), "attention launch");
   if (rc) return rc;

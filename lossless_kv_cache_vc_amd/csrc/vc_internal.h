@@ -105,6 +105,7 @@ struct Plan {
   int head_dim = 0;
   int has_verify = 0;  // the launch holds verifying / drafting requests (over all of them, not
   int has_draft = 0;   // only the ones the kernel arguments carry)
+  int draft_bits = 0;  // bits of every drafting request's pool (16, 2 or 4), -1 if they differ
 };
 int plan_attn(const vc_shape* s, int nreq, const vc_req* reqs, int npools, const vc_pool* pools,
               int split_pages, AttnArgs* args, Plan* plan, std::vector<ReqDev>* table);
