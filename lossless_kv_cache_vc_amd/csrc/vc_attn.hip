@@ -1144,7 +1144,7 @@ struct DRing {
   static constexpr int kPage = kBlock * D * 2;  // bytes of one K or V page
   static constexpr int kSlot = 2 * kPage;       // one page of keys then one of values
   static constexpr int kLoads = kPage / 1024;   // 16-byte-per-lane loads per page and tensor
-  static constexpr int kRing = 16 * kSlot;      // LDS of all waves' rings (4 x 4 or 8 x 2 slots)
+  static constexpr int kRing = 16 * kSlot;      // LDS the rings may take (8 waves x 2 slots in a mixed launch)
   static constexpr int kIds = kRing;
   static constexpr int kBytes = kRing + kMaxChunkPages * 4;
 };
@@ -1207,10 +1207,16 @@ __device__ __forceinline__ u32x2 mask_tokens4(u32x2 v, int first, int valid) {
   return v;
 }
 
+// LDS of a bf16 draft work-group of NW waves with STG ring slots each: the rings, then the page
+// ids of the item
+template <int D, int NW, int STG>
+constexpr int draft_bf16_lds() { return NW * STG * DRing<D>::kSlot + kMaxChunkPages * 4; }
+
 template <int D, int NW, int STG>
 __device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   using R = DRing<D>;
   static_assert(NW * STG * R::kSlot <= R::kRing, "draft rings exceed their LDS");
+  constexpr int kIdsOff = NW * STG * R::kSlot;
   constexpr int NS = D / 32;  // k-steps of the score product
   constexpr int ND = D / 16;  // 16-wide d blocks of the output
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
@@ -1228,7 +1234,7 @@ __device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 #pragma unroll
     for (int s = 0; s < NS; ++s) qreg[s] = row_ok ? ld16(qp + 32 * s + 8 * kg) : u32x4{0, 0, 0, 0};
   }
-  int32_t* ids = reinterpret_cast<int32_t*>(smem + R::kIds);
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + kIdsOff);
   {
     const PoolDev& pl = it.pool;
     const int32_t* pt = pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo;
@@ -2084,11 +2090,13 @@ __global__ __launch_bounds__(kWThreads) void verify_wide_kernel(const AttnArgs a
 // Draft items only, one pool (so one bit width) per launch: 4 waves that split the item's keys.
 template <int D>
 __global__ __launch_bounds__(kDThreads) void draft_bf16_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DRing<D>::kBytes];
+  // two slots per wave: 72 KB at d = 128, so two work-groups share a CU and one streams while the
+  // other starts or finishes an item (four slots, one work-group per CU, was 1 % slower)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[draft_bf16_lds<D, kDWaves, 2>()];
   ItemCtx it;
   int rg;
   if (!decode_item(a, &it, &rg)) return;
-  draft_bf16_item<D, kDWaves, 4>(a, it, smem);
+  draft_bf16_item<D, kDWaves, 2>(a, it, smem);
 }
 
 template <int D, int BITS>
