@@ -1794,9 +1794,13 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   f32x4 acc_o[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc_o[i] = f32x4{};
-  f32x4 vb[NGQ];  // value bias of each channel group: sum_t p_t (z_t - offsets s_t), per column
+  f32x4 vb[NGQ];  // offset part of each channel group's value bias: -sum_t off_t s_t p_t, per column
 #pragma unroll
   for (int i = 0; i < NGQ; ++i) vb[i] = f32x4{};
+  // zero part of the value biases, sum_t z_t,g p_t, of every group in one product: A-operand row m
+  // (this lane's n) holds the zeros of group m % NGQ, so output row g of column n is group g's
+  f32x4 vzs = f32x4{};
+  const int zrow = n % NGQ;
   const u32x4 noff = neg_offsets<BITS>();
   const Expand<BITS> ex;
   float m_run = -INFINITY, l_run = 0.f;
@@ -1889,6 +1893,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       for (int i = 0; i < ND; ++i) acc_o[i] *= alpha;
 #pragma unroll
       for (int i = 0; i < NGQ; ++i) vb[i] *= alpha;
+      vzs *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -1904,17 +1909,16 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     // ---- value side: P'_g = p * scale_t,g; bias_g += sum_t (z_t,g p_t - off_t P'_t,g)
     const uint16_t* vsz = reinterpret_cast<const uint16_t*>(slot + R::kOffVsz + vpage * R::kVsz) + vtok0;
     const uint8_t* vcodes = slot + R::kOffV;
+    {
+      u32x4 vz = ld16(vsz + (2 * zrow + 1) * kBlock);
+      if (!full) vz = mask_tokens(vz, vtok0, vpage ? v1 : v0);  // tokens past the valid ones: no zero
+      vzs = mfma16<true>(vz, p16, vzs);
+    }
 #pragma unroll
     for (int gq = 0; gq < NGQ; ++gq) {
       u32x4 vs = ld16(vsz + (2 * gq) * kBlock);
-      u32x4 vz = ld16(vsz + (2 * gq + 1) * kBlock);
-      if (!full) {  // tokens past the page's valid ones may hold any bits: no scale, no zero
-        const int valid = vpage ? v1 : v0;
-        vs = mask_tokens(vs, vtok0, valid);
-        vz = mask_tokens(vz, vtok0, valid);
-      }
+      if (!full) vs = mask_tokens(vs, vtok0, vpage ? v1 : v0);  // tokens past the valid ones: no scale
       const u32x4 pv = mul_f16x8(p16, vs);
-      vb[gq] = mfma16<true>(vz, p16, vb[gq]);
       vb[gq] = mfma16<true>(noff, pv, vb[gq]);
       // O^T += V^T P'^T for the two 16-channel blocks of this group
 #pragma unroll
@@ -1952,11 +1956,14 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   for (; k < k_full; ++k) step(k, k % STG, std::true_type{});
   for (; k < mine; ++k) step(k, k % STG, std::false_type{});
 
-  // the value bias joins the outputs before any pair that rescales without it
+  // the value bias joins the outputs before any pair that rescales without it; the zero part of
+  // group g for column n is element g of lane n's accumulator (output row g)
 #pragma unroll
   for (int gq = 0; gq < NGQ; ++gq) {
-    acc_o[2 * gq] += vb[gq];
-    acc_o[2 * gq + 1] += vb[gq];
+    const float z = __shfl(vzs[gq], n, 64);
+    const f32x4 bias = vb[gq] + f32x4{z, z, z, z};
+    acc_o[2 * gq] += bias;
+    acc_o[2 * gq + 1] += bias;
   }
   // pairs outside the ring: an odd last context page and the drafted block
   const int npairs = (it.npages + 1) >> 1;
