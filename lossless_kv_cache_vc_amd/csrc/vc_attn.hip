@@ -1213,7 +1213,7 @@ template <int D, int NW, int STG>
 constexpr int draft_bf16_lds() { return NW * STG * DRing<D>::kSlot + kMaxChunkPages * 4; }
 
 template <int D, int NW, int STG>
-__device__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
+__device__ __forceinline__ void draft_bf16_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   using R = DRing<D>;
   static_assert(NW * STG * R::kSlot <= R::kRing, "draft rings exceed their LDS");
   constexpr int kIdsOff = NW * STG * R::kSlot;
@@ -1674,28 +1674,38 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
-template <int D, int BITS, int NW>
+// RP: query rows padded to 4, 8 or 16 (rows_total <= RP).  The 16 columns of the MFMAs are
+// 16 / RP slots of RP columns, and every slot holds the same query rows: the scores and softmax
+// weights of a column depend only on its row.  The value product then takes, in slot j of its
+// B operand, the weights scaled for channel group j (of the set), so one operand serves 16 / RP
+// groups; for a 16-channel output block only the slot of its group is kept, and the join moves
+// that slot to columns 0 .. RP - 1.
+template <int D, int BITS, int NW, int RP>
 __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   using R = KRing<D, BITS, NW>;
   constexpr int STG = R::kStg;
   static_assert(STG >= 2, "KIVI draft ring needs two slots per wave");
+  static_assert(RP == 4 || RP == 8 || RP == 16, "rows padded to 4, 8 or 16");
   constexpr int NS = D / 32;              // k-steps of the score product
   constexpr int ND = D / 16;              // 16-wide channel blocks of the output
   constexpr int NGQ = D / 32;             // value channel groups
+  constexpr int SL = 16 / RP;             // column slots
+  constexpr int NB = (NGQ + SL - 1) / SL; // value operands (sets of SL groups)
   constexpr int KW = (D / 4) * BITS / 32; // words of a key row held by one lane (its D/4 channels)
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const ReqDev& rq = it.rq;
   const int G = a.G;
-  const bool row_ok = n < it.rows_total;
-  const int tok = row_ok ? n / G : 0;
+  const int row = n % RP, slot_n = n / RP;  // this column's query row and slot
+  const bool row_ok = row < it.rows_total;
+  const int tok = row_ok ? row / G : 0;
   const int qpos = rq.q0 + tok;
 
-  // query of row n, channels kg * D/4 .. + D/4 (8 per k-step), in fp16
+  // query of this column's row, channels kg * D/4 .. + D/4 (8 per k-step), in fp16
   u32x4 qh[NS];
   {
     const uint16_t* qp = a.q + ((((int64_t)rq.slot * a.L + it.l) * a.xmax + rq.q0 + tok) * a.Hq +
-                                it.g * G + (row_ok ? n % G : 0)) * D;
+                                it.g * G + (row_ok ? row % G : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qh[s] = bf16x8_to_f16x8(row_ok ? ld16(qp + draft_chan<D>(kg, s)) : u32x4{0, 0, 0, 0});
@@ -1794,9 +1804,14 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   f32x4 acc_o[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc_o[i] = f32x4{};
-  f32x4 vb[NGQ];  // offset part of each channel group's value bias: -sum_t off_t s_t p_t, per column
+  // offset part of the value biases, -sum_t off_t s_t,g p_t, per column: operand set b, slot j
+  // holds group b SL + j
+  f32x4 vb[NB];
 #pragma unroll
-  for (int i = 0; i < NGQ; ++i) vb[i] = f32x4{};
+  for (int i = 0; i < NB; ++i) vb[i] = f32x4{};
+  // value scale plane of this lane's group in set 0; set b adds b SL groups (with more than one
+  // set, SL divides NGQ; slots past the last group, with one set, read group slot % NGQ's)
+  const int vs_lane = SL == 1 ? 0 : 2 * (slot_n % NGQ) * kBlock;
   // zero part of the value biases, sum_t z_t,g p_t, of every group in one product: A-operand row m
   // (this lane's n) holds the zeros of group m % NGQ, so output row g of column n is group g's
   f32x4 vzs = f32x4{};
@@ -1892,7 +1907,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
 #pragma unroll
       for (int i = 0; i < ND; ++i) acc_o[i] *= alpha;
 #pragma unroll
-      for (int i = 0; i < NGQ; ++i) vb[i] *= alpha;
+      for (int i = 0; i < NB; ++i) vb[i] *= alpha;
       vzs *= alpha;
       m_run = m_new;
     }
@@ -1914,13 +1929,17 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       if (!full) vz = mask_tokens(vz, vtok0, vpage ? v1 : v0);  // tokens past the valid ones: no zero
       vzs = mfma16<true>(vz, p16, vzs);
     }
+    u32x4 pv;
 #pragma unroll
     for (int gq = 0; gq < NGQ; ++gq) {
-      u32x4 vs = ld16(vsz + (2 * gq) * kBlock);
-      if (!full) vs = mask_tokens(vs, vtok0, vpage ? v1 : v0);  // tokens past the valid ones: no scale
-      const u32x4 pv = mul_f16x8(p16, vs);
-      vb[gq] = mfma16<true>(noff, pv, vb[gq]);
-      // O^T += V^T P'^T for the two 16-channel blocks of this group
+      if (gq % SL == 0) {  // the weights scaled for the next set of groups (slot j: group gq + j)
+        const int b = gq / SL;
+        u32x4 vs = ld16(vsz + vs_lane + 2 * b * SL * kBlock);
+        if (!full) vs = mask_tokens(vs, vtok0, vpage ? v1 : v0);  // tokens past the valid ones: no scale
+        pv = mul_f16x8(p16, vs);
+        vb[b] = mfma16<true>(noff, pv, vb[b]);
+      }
+      // O^T += V^T P'^T for the two 16-channel blocks of this group (its slot of the set)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int db = 2 * gq + h2;
@@ -1957,13 +1976,24 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   for (; k < mine; ++k) step(k, k % STG, std::false_type{});
 
   // the value bias joins the outputs before any pair that rescales without it; the zero part of
-  // group g for column n is element g of lane n's accumulator (output row g)
+  // group g for column n is element g of lane n's accumulator (output row g).  Then each block's
+  // slot moves to columns 0 .. RP - 1 (the rows past RP take other columns' values; no one reads
+  // them).
 #pragma unroll
   for (int gq = 0; gq < NGQ; ++gq) {
     const float z = __shfl(vzs[gq], n, 64);
-    const f32x4 bias = vb[gq] + f32x4{z, z, z, z};
+    const f32x4 bias = vb[gq / SL] + f32x4{z, z, z, z};
     acc_o[2 * gq] += bias;
     acc_o[2 * gq + 1] += bias;
+    if constexpr (SL > 1) {
+      const int src = lane + (gq % SL) * RP;
+      if (gq % SL != 0) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[2 * gq + h2][i] = __shfl(acc_o[2 * gq + h2][i], src, 64);
+      }
+    }
   }
   // pairs outside the ring: an odd last context page and the drafted block
   const int npairs = (it.npages + 1) >> 1;
@@ -1974,6 +2004,14 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   l_run = wave_xor_sum(l_run, 16);
   l_run = wave_xor_sum(l_run, 32);
   draft_merge<D, NW>(a, it, smem, acc_o, m_run, l_run);
+}
+
+// the KIVI draft for the item's row count: four slots of 4 columns, or one of 16 (a variant of
+// two slots for 5 to 8 rows measured no faster, with 4-bit codes: 0.877 against 0.869 ms)
+template <int D, int BITS, int NW>
+__device__ __forceinline__ void draft_kivi_rows(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
+  if (it.rows_total <= 4) draft_kivi_item<D, BITS, NW, 4>(a, it, smem);
+  else draft_kivi_item<D, BITS, NW, 16>(a, it, smem);
 }
 
 // Work item -> (request, row group, split, kv head, layer).  Work-groups are dealt round-robin
@@ -2070,8 +2108,8 @@ template <int D, int NW>
 __device__ __forceinline__ void draft_dispatch(const AttnArgs& a, const ItemCtx& it, uint8_t* smem) {
   const int bits = it.pool.bits;
   if (bits == 16) draft_bf16_item<D, NW, (NW <= 4 ? 4 : 2)>(a, it, smem);
-  else if (bits == 2) draft_kivi_item<D, 2, NW>(a, it, smem);
-  else draft_kivi_item<D, 4, NW>(a, it, smem);
+  else if (bits == 2) draft_kivi_rows<D, 2, NW>(a, it, smem);
+  else draft_kivi_rows<D, 4, NW>(a, it, smem);
 }
 
 // Verify items only: 8 waves, one work-group per CU (the ring takes most of the LDS).
@@ -2112,7 +2150,7 @@ __global__ __launch_bounds__(kKThreads) void draft_kivi_kernel(const AttnArgs a)
   ItemCtx it;
   int rg;
   if (!decode_item(a, &it, &rg)) return;
-  draft_kivi_item<D, BITS, kKWaves>(a, it, smem);
+  draft_kivi_rows<D, BITS, kKWaves>(a, it, smem);
 }
 
 // One launch over a mixed list (drafting and verifying requests of a batch together).
