@@ -365,6 +365,8 @@ struct VerifyState {
   f32x16 acc_o[ND];
   float m_run, l_run, sc;
   float thr;              // headroom before the running maximum moves (rescale_headroom)
+  float lim;              // 2^thr: a lane's tile weights summing below it need no row maxima;
+                          // -1 while the running maximum is unset
   const uint8_t* kv_pool;  // the pool this wave loads from (K for key waves, V for value waves)
   const uint16_t* kv_blk;  // and its drafted-block array
 };
@@ -437,6 +439,19 @@ __device__ __forceinline__ f32x16 verify_scores(const uint8_t* smem, int st, con
 // verify: its waves score a half and consume it in turn).  MASK: the tile holds a partial,
 // missing or drafted-block page (per-key visibility and value masking); otherwise every key of
 // the tile is a visible context key.
+// Move a lane's running maximum to m_new (the work-group's moves are wave-uniform): rescale its
+// sum and accumulators, and take the headroom and the fast-path bound from the rescaled sum.
+template <int D>
+__device__ __forceinline__ void verify_move(VerifyState<D>& vs, float m_new) {
+  const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
+  vs.l_run *= alpha;
+  vs.thr = rescale_headroom(vs.l_run);
+  vs.lim = (m_new == -INFINITY) ? -1.f : __builtin_ldexpf(1.f, (int)vs.thr);
+#pragma unroll
+  for (int i = 0; i < VerifyState<D>::ND; ++i) vs.acc_o[i] *= alpha;
+  vs.m_run = m_new;
+}
+
 template <int D, bool MASK>
 __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>& vs, const uint8_t* smem,
                                                int t, int vst, f32x16 s_acc) {
@@ -456,14 +471,7 @@ __device__ __forceinline__ void verify_consume(const ItemCtx& it, VerifyState<D>
   mloc = half_swap_max(mloc);
   const float sc = vs.sc;
   const float m_new = fmaxf(vs.m_run, mloc * sc);
-  if (__any(m_new > vs.m_run + vs.thr)) {
-    const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
-    vs.l_run *= alpha;
-    vs.thr = rescale_headroom(vs.l_run);
-#pragma unroll
-    for (int i = 0; i < ND; ++i) vs.acc_o[i] *= alpha;
-    vs.m_run = m_new;
-  }
+  if (__any(m_new > vs.m_run + vs.thr)) verify_move(vs, m_new);
   const float m_use = (vs.m_run == -INFINITY) ? 0.f : vs.m_run;
   uint32_t pb[8];
   float ls0 = 0.f, ls1 = 0.f;
@@ -509,19 +517,7 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
     for (int r = 0; r < 16; ++r)
       if (!vkey_visible(r < 8 ? p0 : p1, 8 * h + (r & 7), vs.qpos)) s_acc[r] = -INFINITY;
   }
-  float mloc = max16(s_acc);
-  mloc = half_swap_max(mloc);
   const float sc = vs.sc;
-  const float m_new = fmaxf(vs.m_run, mloc * sc);
-  if (__any(m_new > vs.m_run + vs.thr)) {
-    const float alpha = (vs.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(vs.m_run - m_new);
-    vs.l_run *= alpha;
-    vs.thr = rescale_headroom(vs.l_run);
-#pragma unroll
-    for (int i = 0; i < ND; ++i) vs.acc_o[i] *= alpha;
-    vs.m_run = m_new;
-  }
-  const float m_use = (vs.m_run == -INFINITY) ? 0.f : vs.m_run;
 
   // score operands of tile t + 1, then its MFMA chain beside tile t's exponentials
   const uint8_t* kst = smem + stn * R::kTileK;
@@ -532,9 +528,31 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop[s]), as_bf(vs.qreg[s]), s_nxt, 0, 0, 0);
-  float e[16];
+
+  // Weights relative to the running maximum.  If every lane's weights sum below 2^thr, no score
+  // is more than thr above the running maximum and the maximum stays: the row maxima are taken
+  // (and the move rule applied to them, then the weights taken again after a move) only when
+  // some lane's sum reaches the bound, or its maximum is unset.
+  float e[16], ls[4];
+  auto weights = [&]() {
+    const float m_use = (vs.m_run == -INFINITY) ? 0.f : vs.m_run;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[r], sc, -m_use));
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s_acc[r], sc, -m_use));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[r] = e[r];
+#pragma unroll
+    for (int r = 4; r < 16; ++r) ls[r & 3] += e[r];
+  };
+  weights();
+  if (__any(!((ls[0] + ls[1]) + (ls[2] + ls[3]) < vs.lim))) {
+    float mloc = max16(s_acc);
+    mloc = half_swap_max(mloc);
+    const float m_new = fmaxf(vs.m_run, mloc * sc);
+    if (__any(m_new > vs.m_run + vs.thr)) {
+      verify_move(vs, m_new);
+      weights();
+    }
+  }
 
   // value operands and the value product of tile t
   const uint8_t* vbase = smem + vst * R::kTileK + vs.voff;
@@ -556,9 +574,6 @@ __device__ __forceinline__ f32x16 verify_fused(const ItemCtx& it, VerifyState<D>
     for (int db = 0; db < ND; ++db)
       vs.acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop[pj][db]), as_bf(bv), vs.acc_o[db], 0, 0, 0);
   }
-  float ls[4] = {e[0], e[1], e[2], e[3]};
-#pragma unroll
-  for (int r = 4; r < 16; ++r) ls[r & 3] += e[r];
   vs.l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
   return s_nxt;
@@ -667,6 +682,7 @@ __device__ __forceinline__ void verify_begin(const AttnArgs& a, const ItemCtx& i
   vs.m_run = -INFINITY;
   vs.l_run = 0.f;
   vs.thr = 0.f;
+  vs.lim = -1.f;
 }
 
 // Steady tiles of a verify item whose refills are leading full context tiles, four at a time,
