@@ -45,6 +45,7 @@ constexpr int kKThreads = 64 * kKWaves;
 // verify paths allow the headroom rescale_headroom gives.  fp16 weights (11 bits) keep 8 units.
 constexpr float kRescaleBf16 = 0.0f;
 constexpr float kRescaleF16 = 8.0f;
+constexpr float kLimF16 = 256.0f;  // 2^kRescaleF16
 
 // Verify headroom after a move of the running maximum, from the lane's running sum l (in units of
 // the new maximum): floor(log2 l) - 3, between 0 and 8.  A key that later raises the maximum by
@@ -1835,6 +1836,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   const u32x4 noff = neg_offsets<BITS>();
   const Expand<BITS> ex;
   float m_run = -INFINITY, l_run = 0.f;
+  float lim = -1.f;  // 2^kRescaleF16 once the running maximum is set
   const float sc = a.scale_log2;
   const int vtok0 = 8 * (kg & 1), vpage = kg >> 1;  // this lane's 8 tokens of a pair
 
@@ -1914,27 +1916,38 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       for (int j = 0; j < 8; ++j)
         if (vtok0 + j >= valid) sv[j] = -INFINITY;
     }
-    float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mloc = row_max4(mloc);
-    const float m_new = fmaxf(m_run, mloc * sc);
-    if (__any(m_new > m_run + kRescaleF16)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    // weights against the running maximum; while every lane's weights sum below 2^headroom none
+    // can exceed it, so the row maxima and the move test run only when some sum reaches it (or a
+    // maximum is unset), and the weights are taken again after a move
+    float e[8];
+    auto weights = [&]() {
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-      for (int i = 0; i < ND; ++i) acc_o[i] *= alpha;
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(sv[j], sc, -m_use));
+    };
+    weights();
+    if (__any(!(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])) < lim))) {
+      float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mloc = row_max4(mloc);
+      const float m_new = fmaxf(m_run, mloc * sc);
+      if (__any(m_new > m_run + kRescaleF16)) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) vb[i] *= alpha;
-      vzs *= alpha;
-      m_run = m_new;
+        for (int i = 0; i < ND; ++i) acc_o[i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) vb[i] *= alpha;
+        vzs *= alpha;
+        m_run = m_new;
+        lim = m_new == -INFINITY ? -1.f : kLimF16;
+        weights();
+      }
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     uint32_t ph[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[j], sc, -m_use));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], sc, -m_use));
-      l_run += e0 + e1;
-      ph[j >> 1] = pack_f16(e0, e1);
+      l_run += e[j] + e[j + 1];
+      ph[j >> 1] = pack_f16(e[j], e[j + 1]);
     }
     const u32x4 p16 = {ph[0], ph[1], ph[2], ph[3]};
     // ---- value side: P'_g = p * scale_t,g; bias_g += sum_t (z_t,g p_t - off_t P'_t,g)
