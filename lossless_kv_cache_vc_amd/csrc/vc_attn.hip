@@ -1691,6 +1691,24 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
+// a0 .. a3 by a lane's slot j (0 .. 3)
+__device__ __forceinline__ float sel_slot(float a0, float a1, float a2, float a3, int j) {
+  const float t0 = (j & 1) ? a1 : a0, t1 = (j & 1) ? a3 : a2;
+  return (j & 2) ? t1 : t0;
+}
+// Four slots of 4 columns in each 16-lane row (lane bits 2-3 the slot, 0-1 the row): every lane
+// takes slot J's value of its row.  ds_swizzle in bit-mask mode (within 32 lanes): keep lane bits
+// 0, 1 and 4, set bits 2-3 to J.
+template <int J>
+__device__ __forceinline__ uint32_t slot_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x13 | (J << 7));
+}
+// sum over the four slots of a lane's row (lanes 4 and 8 apart)
+__device__ __forceinline__ float slot_sum4(float x) {
+  x += __shfl_xor(x, 4, 64);
+  return x + __shfl_xor(x, 8, 64);
+}
+
 // RP: query rows padded to 4, 8 or 16 (rows_total <= RP).  The 16 columns of the MFMAs are
 // 16 / RP slots of RP columns, and every slot holds the same query rows: the scores and softmax
 // weights of a column depend only on its row.  The value product then takes, in slot j of its
@@ -1918,15 +1936,28 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     }
     // weights against the running maximum; while every lane's weights sum below 2^headroom none
     // can exceed it, so the row maxima and the move test run only when some sum reaches it (or a
-    // maximum is unset), and the weights are taken again after a move
-    float e[8];
+    // maximum is unset), and the weights are taken again after a move.  With four slots, a lane
+    // takes only tokens 2 j, 2 j + 1 of its 8 (j its slot: the other slots hold the same row) and
+    // gathers the rest from the slots that took them.
+    constexpr int NE = SL == 4 ? 2 : 8;
+    float x[NE], e[NE];
+    if constexpr (SL == 4) {
+      x[0] = sel_slot(sv[0], sv[2], sv[4], sv[6], slot_n);
+      x[1] = sel_slot(sv[1], sv[3], sv[5], sv[7], slot_n);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = sv[j];
+    }
     auto weights = [&]() {
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(sv[j], sc, -m_use));
+      for (int j = 0; j < NE; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[j], sc, -m_use));
     };
     weights();
-    if (__any(!(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])) < lim))) {
+    float esum;
+    if constexpr (SL == 4) esum = e[0] + e[1];
+    else esum = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    if (__any(!(esum < lim))) {
       float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       mloc = row_max4(mloc);
       const float m_new = fmaxf(m_run, mloc * sc);
@@ -1943,13 +1974,18 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
         weights();
       }
     }
-    uint32_t ph[4];
+    u32x4 p16;
+    if constexpr (SL == 4) {
+      l_run += e[0] + e[1];  // this lane's share; the slots' shares are summed after the loop
+      const uint32_t ph = pack_f16(e[0], e[1]);
+      p16 = u32x4{slot_bcast<0>(ph), slot_bcast<1>(ph), slot_bcast<2>(ph), slot_bcast<3>(ph)};
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      l_run += e[j] + e[j + 1];
-      ph[j >> 1] = pack_f16(e[j], e[j + 1]);
+      for (int j = 0; j < 8; j += 2) {
+        l_run += e[j] + e[j + 1];
+        p16[j >> 1] = pack_f16(e[j], e[j + 1]);
+      }
     }
-    const u32x4 p16 = {ph[0], ph[1], ph[2], ph[3]};
     // ---- value side: P'_g = p * scale_t,g; bias_g += sum_t (z_t,g p_t - off_t P'_t,g)
     const uint16_t* vsz = reinterpret_cast<const uint16_t*>(slot + R::kOffVsz + vpage * R::kVsz) + vtok0;
     const uint8_t* vcodes = slot + R::kOffV;
@@ -2024,6 +2060,8 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       }
     }
   }
+  // with four slots each lane summed its slot's tokens only: the row's full share per lane again
+  if constexpr (SL == 4) l_run = slot_sum4(l_run);
   // pairs outside the ring: an odd last context page and the drafted block
   const int npairs = (it.npages + 1) >> 1;
   for (int pp = ring_pairs + w; pp < npairs; pp += NW)
