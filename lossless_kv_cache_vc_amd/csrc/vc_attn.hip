@@ -1821,10 +1821,21 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
     if (R::kParams == 1024 || o16 < R::kParams)
       __builtin_amdgcn_global_load_lds(pbase + po, (lds_ptr_t)(slot + R::kOffKsz), 16, 0, kNontemporal);
   };
+  // page ids of this wave's pair k, straight from the page table: the table is not written while
+  // the kernel runs, so it is read through the constant address space and the uniform index gives
+  // scalar loads into SGPRs; an entry outside the pool loads block 0 (such pages are masked, or
+  // never full, by the validity taken from the table in LDS)
+  using const_i32 = const __attribute__((address_space(4))) int32_t*;
+  const const_i32 pt_k = (const_i32)(pl.page_table + (int64_t)rq.page_row * pl.max_pages + it.p_lo);
+  const uint32_t nblk_u = (uint32_t)pl.nblk;
   auto pair_ids = [&](int k, int& id0, int& id1) {
-    const int pp = w + NW * k;
-    id0 = k < mine ? ids[2 * pp] : 0;
-    id1 = k < mine ? ids[2 * pp + 1] : 0;
+    id0 = id1 = 0;
+    if (k < mine) {
+      const int pp = w + NW * k;
+      const int a0 = pt_k[2 * pp], a1 = pt_k[2 * pp + 1];
+      id0 = (uint32_t)a0 < nblk_u ? a0 : 0;
+      id1 = (uint32_t)a1 < nblk_u ? a1 : 0;
+    }
   };
 #pragma unroll
   for (int k = 0; k < STG - 1; ++k)
