@@ -1865,7 +1865,13 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
   const u32x4 noff = neg_offsets<BITS>();
   const Expand<BITS> ex;
   float m_run = -INFINITY, l_run = 0.f;
-  float lim = -1.f;  // 2^kRescaleF16 once the running maximum is set
+  float lim = -1.f;    // 2^kRescaleF16 once the running maximum is set
+  float m_use = 0.f;   // the running maximum, 0 while unset
+  // The key rows 4..7 of a 16-key half are kKeyStepB bytes further.  The offset is opaque to the
+  // optimiser (set once per item), so the two 8-byte reads of 2-bit codes stay separate
+  // instructions: fused into one paired read, its two halves, 256 bytes apart, would share banks.
+  uint32_t kstep1 = R::kKeyStepB;
+  asm volatile("" : "+v"(kstep1));
   const float sc = a.scale_log2;
   const int vtok0 = 8 * (kg & 1), vpage = kg >> 1;  // this lane's 8 tokens of a pair
 
@@ -1892,11 +1898,8 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       const int tk = 8 * ((n >> 2) & 1) + 4 * b + (n & 3);
       constexpr int LB = 4 * KW;  // bytes of a row this lane reads: one LDS read of that width
       const int ob = kg * LB;
-      // rows 4 b on are kKeyStepB further; the offset is kept opaque so that the two 8-byte reads of
-      // 2-bit codes are not fused into one paired read, whose two halves, 256 bytes apart, would
-      // share banks
-      uint32_t kstep = b * R::kKeyStepB;
-      if (b) asm volatile("" : "+v"(kstep));
+      // rows 4 b on are kKeyStepB further (kstep1, opaque: see its definition)
+      const uint32_t kstep = b ? kstep1 : 0u;
       const uint8_t* kp = slot + R::kcode_pos(n >> 3, tk - 4 * b, ob >> 4) + kstep + (ob & 15);
       uint32_t words[KW];
       if constexpr (KW == 4) {
@@ -1960,7 +1963,6 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
       for (int j = 0; j < 8; ++j) x[j] = sv[j];
     }
     auto weights = [&]() {
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
       for (int j = 0; j < NE; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[j], sc, -m_use));
     };
@@ -1982,6 +1984,7 @@ __device__ void draft_kivi_item(const AttnArgs& a, const ItemCtx& it, uint8_t* s
         vzs *= alpha;
         m_run = m_new;
         lim = m_new == -INFINITY ? -1.f : kLimF16;
+        m_use = m_new == -INFINITY ? 0.f : m_new;
         weights();
       }
     }
