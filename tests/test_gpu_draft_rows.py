@@ -2,9 +2,9 @@
 
 A drafting request covers block positions q0 .. q0 + rows - 1 (rows * G <= 16 query rows per kv
 head); position j sees the compressed context and drafted rows 0 .. j, as the j-th draft step does
-on its own.  The cases put 4 rows (G = 1 and 2: the layout that repeats the rows over four column
-slots), 6, 8 and 16 rows per kv head in one step, over each drafting cache kind, and compare every
-row with the oracle's single steps.
+on its own.  The cases put 3 or 4 rows (G = 1, 2 and 3: the layout that repeats the rows over four
+column slots), 6, 8 and 16 rows per kv head in one step, over each drafting cache kind, and
+compare every row with the oracle's single steps.
 """
 import pytest
 import torch
@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 # (G, rows per request, head dim, drafting cache)
 CASES = [(1, 4, 128, C.COMP_KIVI2), (2, 2, 128, C.COMP_DROP_KIVI4), (2, 2, 64, C.COMP_KIVI2),
          (1, 3, 128, C.COMP_DROP), (2, 3, 128, C.COMP_KIVI2), (4, 2, 128, C.COMP_DROP_KIVI4),
-         (4, 4, 128, C.COMP_DROP), (4, 4, 64, C.COMP_KIVI2)]
+         (4, 4, 128, C.COMP_DROP), (4, 4, 64, C.COMP_KIVI2),
+         # 3 rows per kv head: one column of each 4-column slot holds no row
+         (1, 3, 128, C.COMP_KIVI2), (3, 1, 128, C.COMP_DROP_KIVI4)]
 
 
 def _cfg(G, d, comp, case):
