@@ -104,13 +104,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(int max_x, int max_
 // z = o * W_u on bf16 MFMA with fp32 accumulation.  Each fp32 element x of o is split into
 // bf16 hi = RNE(x) and lo = RNE(x - hi) (x - hi is exact in fp32, so |x - hi - lo| <= 2^-18 |x|);
 // W_u is bf16, so hi * w and lo * w are exact in fp32 and z carries only fp32 accumulation error.
-// A work-group of 4 waves computes a 128 x 128 tile of z, each wave 64 x 64 (2 x 2 blocks of
-// 32 x 32, v_mfma_f32_32x32x16_bf16), over K steps of 32 staged in LDS: o as hi and lo [m][k],
+// A work-group of 4 waves computes a 128 x 256 tile of z, each wave 64 x 128 (2 x 4 blocks of
+// 32 x 32, v_mfma_f32_32x32x16_bf16, so each LDS operand read feeds 2 to 8 products), over K
+// steps of 32 staged in LDS: o as hi and lo [m][k],
 // W_u transposed to [n][k], so every MFMA operand is one 16-byte LDS read; rows are padded to 40
 // bf16 (80 bytes) so the reads of a 32-lane half fall on distinct banks.  The next K step's
 // global loads are issued into registers before this step's MFMAs.  VEC: o rows, W_u rows and
 // the bases allow 16-byte global loads.
-constexpr int kLM = 128, kLN = 128, kLK = 32, kLPad = 40;
+constexpr int kLM = 128, kLN = 256, kLK = 32, kLPad = 40;
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
@@ -120,7 +121,7 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // and two k rows of 8 consecutive W_u entries (k 2kp, 2kp + 1; n nq..nq+7).
 struct LogitsTile {
   float o[4][4];
-  uint32_t w[2][4];
+  uint32_t w[2][kLN / 128][4];  // [k row][128-column half][packed pairs]
 };
 
 template <bool VEC>
@@ -144,22 +145,24 @@ __device__ __forceinline__ void logits_fetch(LogitsTile& t, int rows, int width,
   }
   const int kp = tid % (kLK / 2), nq = (tid / (kLK / 2)) * 8;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int gk = k0 + 2 * kp + r, gn = n0 + nq;
-    if constexpr (VEC) {  // vocab % 8 == 0
-      const u32x4 v = (gk < width && gn < vocab) ? *reinterpret_cast<const u32x4*>(wu + (int64_t)gk * vocab + gn)
-                                                 : u32x4{0, 0, 0, 0};
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) t.w[r][j] = v[j];
-    } else {
+    for (int hf = 0; hf < kLN / 128; ++hf) {
+      const int gk = k0 + 2 * kp + r, gn = n0 + 128 * hf + nq;
+      if constexpr (VEC) {  // vocab % 8 == 0
+        const u32x4 v = (gk < width && gn < vocab) ? *reinterpret_cast<const u32x4*>(wu + (int64_t)gk * vocab + gn)
+                                                   : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (gk < width && gn + 2 * j < vocab) ? wu[(int64_t)gk * vocab + gn + 2 * j] : 0;
-        const uint32_t hi = (gk < width && gn + 2 * j + 1 < vocab) ? wu[(int64_t)gk * vocab + gn + 2 * j + 1] : 0;
-        t.w[r][j] = lo | (hi << 16);
+        for (int j = 0; j < 4; ++j) t.w[r][hf][j] = v[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = (gk < width && gn + 2 * j < vocab) ? wu[(int64_t)gk * vocab + gn + 2 * j] : 0;
+          const uint32_t hi = (gk < width && gn + 2 * j + 1 < vocab) ? wu[(int64_t)gk * vocab + gn + 2 * j + 1] : 0;
+          t.w[r][hf][j] = lo | (hi << 16);
+        }
       }
     }
-  }
 }
 
 // o as bf16 hi and lo parts [m][k]; W_u transposed [n][k], the thread's two k rows packed into
@@ -184,11 +187,13 @@ __device__ __forceinline__ void logits_stage(const LogitsTile& t, uint16_t* s_hi
   }
   const int kp = tid % (kLK / 2), nq = (tid / (kLK / 2)) * 8;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w0 = (t.w[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    const uint32_t w1 = (t.w[1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    *reinterpret_cast<uint32_t*>(s_w + (nq + j) * kLPad + 2 * kp) = w0 | (w1 << 16);
-  }
+  for (int hf = 0; hf < kLN / 128; ++hf)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w0 = (t.w[0][hf][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t w1 = (t.w[1][hf][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      *reinterpret_cast<uint32_t*>(s_w + (128 * hf + nq + j) * kLPad + 2 * kp) = w0 | (w1 << 16);
+    }
 }
 
 template <bool VEC>
@@ -199,13 +204,14 @@ __global__ __launch_bounds__(256) void logits_kernel(int rows, int width, int vo
   __shared__ __attribute__((aligned(16))) uint16_t s_w[kLN * kLPad];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int m0 = blockIdx.y * kLM, n0 = blockIdx.x * kLN;
-  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;  // this wave's 64 x 64 part of the tile
+  constexpr int NJ = kLN / 64;  // 32-column blocks of a wave
+  const int wm = (w & 1) * 64, wn = (w >> 1) * (kLN / 2);  // this wave's 64 x kLN/2 part of the tile
   const int r32 = lane & 31, kh = lane >> 5;
-  f32x16 acc[2][2];
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   LogitsTile t;
   logits_fetch<VEC>(t, rows, width, vocab, o, ld_o, wu, m0, n0, 0);
   for (int k0 = 0; k0 < width; k0 += kLK) {
@@ -216,17 +222,18 @@ __global__ __launch_bounds__(256) void logits_kernel(int rows, int width, int vo
 #pragma unroll
     for (int ks = 0; ks < kLK / 16; ++ks) {
       const int kc = ks * 16 + kh * 8;  // lane's 8 k of this 16-k step
-      u32x4 ah[2], al[2], bw[2];
+      u32x4 ah[2], al[2], bw[NJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         ah[i] = *reinterpret_cast<const u32x4*>(s_hi + (wm + 32 * i + r32) * kLPad + kc);
         al[i] = *reinterpret_cast<const u32x4*>(s_lo + (wm + 32 * i + r32) * kLPad + kc);
-        bw[i] = *reinterpret_cast<const u32x4*>(s_w + (wn + 32 * i + r32) * kLPad + kc);
       }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bw[j] = *reinterpret_cast<const u32x4*>(s_w + (wn + 32 * j + r32) * kLPad + kc);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
                                                               __builtin_bit_cast(bf16x8, bw[j]), acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al[i]),
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(256) void logits_kernel(int rows, int width, int vo
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int gn = n0 + wn + 32 * j + r32;
       if (gn >= vocab) continue;
 #pragma unroll
