@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("rows,width,ld_o,vocab", [
-    (200, 256, 256, 384),     # 16-byte loads, 2 x 3 tiles with ragged rows
+    (200, 256, 256, 384),     # 16-byte loads, 2 x 2 tiles (128 x 256), ragged rows and vocabulary
     (130, 64, 72, 136),       # 16-byte loads, row stride > width
     (75, 100, 104, 203),      # scalar loads: vocab % 8 != 0, width % 32 != 0
     (1, 4096, 4096, 4096),    # one row at the 8B shape's width and vocabulary
